@@ -1,0 +1,172 @@
+"""KDA prefill oracle -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library
+(``kda_recurrent_state_amd``) never imports it and shares no code with it.
+
+What it provides (fp64, plain loops in ``kda_oracle.c``):
+
+* :func:`state_gather` / :func:`state_scatter` -- the state-copy contract of
+  the page "vllm-ascend 的 KDA 状态复制 Triton 集成" (section "数值契约"):
+  invalid or negative indices and false flags gather zeros, scatter skips
+  invalid targets and ignores flags, page gaps and storage offsets are never
+  touched.  Raw bits are copied.
+* :func:`kda_recurrence` -- the gated delta rule token by token,
+  S_t = (I - beta_t k_t k_t^T) Diag(exp g_t) S_{t-1} + beta_t k_t v_t^T,
+  o_t = scale * S_t^T q_t, over a varlen batch (page
+  "【轻量化复刻大模型 / KIMI K3】KDA 对 AI Infra 的挑战与各家应对", section 1.1).
+* :mod:`oracle.chunk_form` -- the same map evaluated through the chunk
+  decomposition stages of "PR #33465 完整报告" (section "关键源码片段"), in
+  fp64 numpy; used to pin the chunk formulas, never by the product path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+L2NORM_EPS = 1e-6
+
+
+def build(force: bool = True) -> str:
+    """Compile kda_oracle.c with gcc (-O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp",
+                               "-fno-fast-math", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        i64, vp, dp = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p
+        lib.oracle_state_gather.argtypes = [vp, i64, i64, i64, i64, i64, vp, vp, ctypes.c_int, i64, vp, vp]
+        lib.oracle_state_gather.restype = ctypes.c_int
+        lib.oracle_state_scatter.argtypes = [vp, i64, i64, i64, i64, i64, vp, vp, ctypes.c_int, i64, vp]
+        lib.oracle_state_scatter.restype = ctypes.c_int
+        lib.oracle_kda_recurrence.argtypes = [i64, i64, i64, i64, vp, dp, dp, dp, dp, dp, dp,
+                                              ctypes.c_double, ctypes.c_int, ctypes.c_double, dp, dp,
+                                              ctypes.c_int]
+        lib.oracle_kda_recurrence.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _raw_dtype(elem_bytes: int):
+    if elem_bytes == 4:
+        return np.uint32
+    if elem_bytes == 2:
+        return np.uint16
+    raise ValueError("elem_bytes must be 2 or 4")
+
+
+def state_gather(backing: np.ndarray, offset: int, shape, strides, indices: np.ndarray,
+                 flags: np.ndarray | None) -> np.ndarray:
+    """Gather rows of a cache view into a packed [S,H,V,K] array of raw bits.
+
+    ``backing`` is the whole allocation as a 1-D uint32 (fp32) or uint16
+    (bf16) array; the cache view starts ``offset`` elements in and has the
+    given ``shape`` (num_rows, H, V, K) and element ``strides``.
+    """
+    lib = _load()
+    backing = np.ascontiguousarray(backing)
+    eb = backing.dtype.itemsize
+    nrows, H, V, K = (int(x) for x in shape)
+    st = np.asarray(strides, dtype=np.int64)
+    idx = np.ascontiguousarray(indices)
+    if idx.dtype not in (np.int32, np.int64):
+        raise TypeError("indices must be int32 or int64")
+    S = idx.shape[0]
+    packed = np.empty((S, H, V, K), dtype=_raw_dtype(eb))
+    fl = None if flags is None else np.ascontiguousarray(flags.astype(np.uint8))
+    base = backing.ctypes.data + int(offset) * eb
+    rc = lib.oracle_state_gather(base, eb, nrows, H, V, K, _ptr(st), _ptr(idx), int(idx.dtype == np.int64),
+                                 S, None if fl is None else _ptr(fl), _ptr(packed))
+    if rc != 0:
+        raise RuntimeError("oracle_state_gather failed: %d" % rc)
+    return packed
+
+
+def state_scatter(backing: np.ndarray, offset: int, shape, strides, indices: np.ndarray,
+                  packed: np.ndarray) -> np.ndarray:
+    """Return a copy of ``backing`` with the valid packed rows written to the cache view."""
+    lib = _load()
+    out = np.array(backing, copy=True)
+    eb = out.dtype.itemsize
+    nrows, H, V, K = (int(x) for x in shape)
+    st = np.asarray(strides, dtype=np.int64)
+    idx = np.ascontiguousarray(indices)
+    if idx.dtype not in (np.int32, np.int64):
+        raise TypeError("indices must be int32 or int64")
+    pk = np.ascontiguousarray(packed).view(_raw_dtype(eb))
+    S = idx.shape[0]
+    if pk.shape != (S, H, V, K):
+        raise ValueError("packed shape mismatch")
+    base = out.ctypes.data + int(offset) * eb
+    rc = lib.oracle_state_scatter(base, eb, nrows, H, V, K, _ptr(st), _ptr(idx), int(idx.dtype == np.int64),
+                                  S, _ptr(pk))
+    if rc != 0:
+        raise RuntimeError("oracle_state_scatter: duplicate valid scatter targets (precondition)")
+    return out
+
+
+def kda_recurrence(q, k, v, g, beta, cu_seqlens, initial=None, scale=None, use_l2norm=True,
+                   eps=L2NORM_EPS, threads=1):
+    """Token-by-token gated delta rule in fp64.
+
+    q, k, g: [T,H,K]; v: [T,H,V]; beta: [T,H]; cu_seqlens: [N+1];
+    initial: [N,H,V,K] or None.  ``scale`` defaults to K**-0.5.
+    Returns (out [T,H,V], final_state [N,H,V,K]) as float64 arrays.
+    """
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    g = np.ascontiguousarray(g, dtype=np.float64)
+    beta = np.ascontiguousarray(beta, dtype=np.float64)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+    T, H, K = q.shape
+    V = v.shape[2]
+    N = cu.shape[0] - 1
+    if k.shape != (T, H, K) or g.shape != (T, H, K) or v.shape[:2] != (T, H) or beta.shape != (T, H):
+        raise ValueError("shape mismatch")
+    if N < 0 or cu[0] != 0 or cu[-1] != T:
+        raise ValueError("cu_seqlens must start at 0 and end at T")
+    init = None
+    if initial is not None:
+        init = np.ascontiguousarray(initial, dtype=np.float64)
+        if init.shape != (N, H, V, K):
+            raise ValueError("initial state shape mismatch")
+    if scale is None:
+        scale = K ** -0.5
+    out = np.zeros((T, H, V), dtype=np.float64)
+    fin = np.zeros((N, H, V, K), dtype=np.float64)
+    rc = lib.oracle_kda_recurrence(N, H, K, V, _ptr(cu), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                   None if init is None else _ptr(init), float(scale), int(bool(use_l2norm)),
+                                   float(eps), _ptr(out), _ptr(fin), int(threads))
+    if rc != 0:
+        raise RuntimeError("oracle_kda_recurrence failed: %d" % rc)
+    return out, fin
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
