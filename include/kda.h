@@ -1,0 +1,197 @@
+/*
+ * kda.h -- C ABI of the KDA (Kimi Delta Attention) prefill hot path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The prefill step has three stages:
+ *   1. kda_state_gather   -- copy each request's initial recurrent state out
+ *                            of indexed rows of a state cache;
+ *   2. kda_chunk_prefill  -- run the chunkwise gated delta rule (chunk size
+ *                            64) over a varlen batch delimited by cu_seqlens;
+ *   3. kda_state_scatter  -- copy the final states back into cache rows.
+ *
+ * Sources (web pages, cited by title and section):
+ *  [P1] "vllm-ascend 的 KDA 状态复制 Triton 集成：PR 17301 对齐的预编译 worker
+ *       生命周期方案": section "背景" (gather -> chunk math -> scatter around
+ *       an unchanged chunk kernel with chunk size 64), section "数值契约"
+ *       (the copy contract), section "自动分发" (the layout admissibility
+ *       rule), section "启动准备" (index dtype kept as given).
+ *  [P2] "【轻量化复刻大模型 / KIMI K3】KDA 对 AI Infra 的挑战与各家应对",
+ *       section 1.1 (S_t = M_t S_{t-1} + b_t) and the varlen row of the
+ *       table in section 0x00 (cu_seqlens, every sequence advances its own
+ *       state).
+ *  [P3] "PR #33465 完整报告" (SGLang Kimi-K3 on NPU), section "关键源码片段":
+ *       the prefill decomposition l2norm -> chunk-local cumulative gate sum
+ *       (scaled by log2 e) -> gated K K^T -> triangular solve -> W/U
+ *       recompute -> inter-chunk state recurrence -> chunk output, with scale
+ *       K^-1/2 and the output allowed to reuse v's buffer.
+ *
+ * Conventions shared by every entry point:
+ *  - Ownership: the library owns no memory.  The caller allocates every
+ *    buffer (device memory unless stated) and passes the HIP stream on each
+ *    call; nothing is retained between calls.
+ *  - stream: a hipStream_t passed as void* (NULL = the default stream).  All
+ *    work is enqueued on it; no entry point synchronises the device or reads
+ *    device memory on the host.
+ *  - Validation is host-only and fail-closed: a bad argument returns an error
+ *    status and enqueues nothing.
+ *  - Errors from the HIP runtime return KDA_E_HIP; kda_last_error_detail()
+ *    then names the failing call (thread-local, valid until the next call on
+ *    the same thread).
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
+typedef enum { KDA_I32 = 0, KDA_I64 = 1 } kda_index_t;
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_E_NULL = 1,        /* a required pointer is NULL                                   */
+  KDA_E_DTYPE = 2,       /* dtype / index type outside the supported set                 */
+  KDA_E_SHAPE = 3,       /* negative or zero size where a positive one is required       */
+  KDA_E_LAYOUT = 4,      /* cache inner dims [H,V,K] are not dense                       */
+  KDA_E_OVERLAP = 5,     /* cache row stride smaller than the row payload (pages overlap) */
+  KDA_E_UNSUPPORTED = 6, /* a size this build has no kernel for (e.g. K > 128)            */
+  KDA_E_WORKSPACE = 7,   /* workspace missing or smaller than kda_chunk_prefill_workspace_size */
+  KDA_E_ALIAS = 8,       /* output partially overlaps an input                          */
+  KDA_E_HIP = 9          /* the HIP runtime reported an error                           */
+} kda_status_t;
+
+/*
+ * A view of one layer's recurrent-state cache: a 4-D tensor [num_rows, H, V, K].
+ * Element (r, h, v, c) is S_h[c][v] of cache row r, where S_h is the K x V
+ * state of head h (state rows are laid out [H][V][K], K fastest; [P1] section
+ * "自动分发" gives the [N,H,V,K] shape).
+ *  data      -- address of element (0,0,0,0): the storage offset is already
+ *               applied (a tensor's data_ptr()).
+ *  dtype     -- KDA_F32 or KDA_BF16.
+ *  stride[4] -- element strides of the four dims.
+ * Admissible layouts ([P1] section "自动分发"): num_rows > 0, H, V, K > 0;
+ * reading the inner dims from the back, each has size 1 or a stride equal to
+ * the running payload (stride[3] = 1, stride[2] = K, stride[1] = V*K); and
+ * stride[0] >= H*V*K, so rows never overlap.  The gap between a row's payload
+ * and the next row is never read or written, nor is anything before data.
+ */
+typedef struct {
+  void* data;
+  kda_dtype_t dtype;
+  int64_t num_rows, H, V, K;
+  int64_t stride[4];
+} kda_state_cache_t;
+
+/*
+ * kda_state_gather -- [P1] section "数值契约", gather side.
+ * For i in [0, num_selected):
+ *   packed[i] = cache row indices[i]   if 0 <= indices[i] < num_rows and
+ *                                       (flags == NULL or flags[i] != 0),
+ *   packed[i] = all-zero bits           otherwise.
+ *  indices     -- device array of num_selected int32 (KDA_I32) or int64
+ *                 (KDA_I64) values, read in their own width (no conversion).
+ *                 Duplicates are allowed.
+ *  flags       -- device array of num_selected bytes, or NULL (all true).
+ *  packed      -- device output [num_selected, H, V, K], contiguous, in the
+ *                 cache dtype; every row is written.
+ * Bits are copied unchanged.  num_selected == 0 validates the cache view and
+ * enqueues nothing.  Preconditions (not checked): packed does not overlap the
+ * cache.  Errors: KDA_E_NULL, KDA_E_DTYPE, KDA_E_SHAPE, KDA_E_LAYOUT,
+ * KDA_E_OVERLAP, KDA_E_HIP.
+ */
+kda_status_t kda_state_gather(const kda_state_cache_t* cache, const void* indices, kda_index_t index_type,
+                              int64_t num_selected, const uint8_t* flags, void* packed, void* stream);
+
+/*
+ * kda_state_scatter -- [P1] section "数值契约", scatter side.
+ * For i in [0, num_selected): if 0 <= indices[i] < num_rows, cache row
+ * indices[i] = packed[i]; other entries are skipped.  Initial-state flags
+ * play no part: a valid target is always written.
+ *  packed      -- device input [num_selected, H, V, K], contiguous, cache
+ *                 dtype (convert final states to the cache dtype first).
+ * Preconditions (not checked, no device-to-host scan): valid targets are
+ * unique; packed does not overlap the cache.  num_selected == 0 enqueues
+ * nothing.  Errors as for kda_state_gather.
+ */
+kda_status_t kda_state_scatter(const kda_state_cache_t* cache, const void* indices, kda_index_t index_type,
+                               int64_t num_selected, const void* packed, void* stream);
+
+/*
+ * Arguments of kda_chunk_prefill.  All pointers are device pointers to
+ * contiguous row-major arrays.
+ *  T, N, H, K, V   -- tokens, sequences, heads, key dim (1..128), value dim (>= 1).
+ *  q, k            -- [T, H, K] in qkv_dtype.           v -- [T, H, V] in qkv_dtype.
+ *  g               -- [T, H, K] fp32: natural-log decay per key channel; the
+ *                     state is multiplied by exp(g) (g <= 0 for a decay).
+ *  beta            -- [T, H] in beta_dtype (fp32 or bf16).
+ *  cu_seqlens      -- [N+1] int32 token offsets; sequence n is tokens
+ *                     [cu_seqlens[n], cu_seqlens[n+1]).  Precondition (not
+ *                     checked on the host): cu_seqlens[0] = 0, non-decreasing,
+ *                     cu_seqlens[N] = T; the kernels clamp so that bad
+ *                     offsets cannot address outside [0, T).
+ *  initial_state   -- [N, H, V, K] in initial_dtype, element (n,h,v,c) =
+ *                     S[c][v]; or NULL for zero initial states.
+ *  out             -- [T, H, V] in qkv_dtype.  It may be exactly v (the
+ *                     output then overwrites v, [P3]); any other overlap
+ *                     with an input is an error.
+ *  final_state     -- [N, H, V, K] in final_dtype, or NULL.  fp32 states are
+ *                     rounded to bf16 to nearest even when final_dtype is bf16.
+ *  scale           -- read-out scale ([P3] uses K^-1/2).
+ *  use_qk_l2norm   -- nonzero: q and k rows are divided by sqrt(|x|^2 + 1e-6).
+ *  workspace       -- device scratch of at least
+ *                     kda_chunk_prefill_workspace_size(T, N, H, K, V) bytes
+ *                     (may be NULL when that size is 0).
+ * Per sequence n and head h, with S the K x V fp32 state, this computes for
+ * each token t in order ([P2] section 1.1 and the gated delta rule):
+ *   S <- (I - beta_t k_t k_t^T) Diag(exp g_t) S + beta_t k_t v_t^T
+ *   out_t = scale * S^T q_t
+ * evaluated chunkwise in chunks of 64 tokens aligned to each sequence start
+ * ([P3]).  Sequences of length 0 pass their initial state through.
+ */
+typedef struct {
+  int64_t T, N, H, K, V;
+  const void* q;
+  const void* k;
+  const void* v;
+  kda_dtype_t qkv_dtype;
+  const float* g;
+  const void* beta;
+  kda_dtype_t beta_dtype;
+  const int32_t* cu_seqlens;
+  const void* initial_state;
+  kda_dtype_t initial_dtype;
+  void* out;
+  void* final_state;
+  kda_dtype_t final_dtype;
+  float scale;
+  int use_qk_l2norm;
+  void* workspace;
+  size_t workspace_bytes;
+} kda_prefill_args_t;
+
+/* Bytes of device workspace kda_chunk_prefill needs for these sizes. */
+size_t kda_chunk_prefill_workspace_size(int64_t T, int64_t N, int64_t H, int64_t K, int64_t V);
+
+/*
+ * kda_chunk_prefill -- the chunkwise gated delta rule of [P3] over a varlen
+ * batch; see kda_prefill_args_t for arguments and semantics.
+ * N == 0 enqueues nothing.  Errors: KDA_E_NULL, KDA_E_DTYPE, KDA_E_SHAPE,
+ * KDA_E_UNSUPPORTED, KDA_E_WORKSPACE, KDA_E_ALIAS, KDA_E_HIP.
+ */
+kda_status_t kda_chunk_prefill(const kda_prefill_args_t* args, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* kda_status_string(kda_status_t status);
+
+/* Detail of the last KDA_E_HIP on this thread ("" if none). */
+const char* kda_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

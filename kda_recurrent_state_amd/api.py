@@ -1,0 +1,196 @@
+"""Python binding of libkda with the C ABI's names.
+
+Argument marshalling only: tensors are described by pointer, dtype, sizes and
+strides and handed to the C entry points together with the current HIP
+stream.  Every step of the path runs in libkda's kernels; PyTorch supplies
+device memory and streams.  A non-OK status raises :class:`KDAError`.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import KDA_BF16, KDA_F32, KDA_I32, KDA_I64, KDAError, PrefillArgs, StateCache
+
+_DT = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
+
+
+def _dtype_code(t: torch.Tensor, what: str) -> int:
+    if t.dtype not in _DT:
+        raise KDAError(what, 2, "dtype %s (need float32 or bfloat16)" % t.dtype)
+    return _DT[t.dtype]
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libkda works on device tensors; got a %s tensor" % t.device)
+
+
+def cache_descriptor(cache: torch.Tensor) -> StateCache:
+    """Describe a 4-D [num_rows, H, V, K] cache view (storage offset included in data_ptr)."""
+    if cache.dim() != 4:
+        raise KDAError("kda_state_cache", 3, "cache must be 4-D [num_rows, H, V, K]")
+    d = StateCache()
+    d.data = cache.data_ptr()
+    d.dtype = _DT.get(cache.dtype, 99)
+    d.num_rows, d.H, d.V, d.K = (int(x) for x in cache.shape)
+    for i, s in enumerate(cache.stride()):
+        d.stride[i] = int(s)
+    return d
+
+
+def _index_code(indices: torch.Tensor) -> int:
+    if indices.dtype == torch.int32:
+        return KDA_I32
+    if indices.dtype == torch.int64:
+        return KDA_I64
+    raise KDAError("state copy", 2, "indices must be int32 or int64")
+
+
+def kda_state_gather(cache: torch.Tensor, indices: torch.Tensor, flags: Optional[torch.Tensor] = None,
+                     packed: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """packed[i] = cache[indices[i]] if valid and flagged, else zeros (all rows written)."""
+    lib = _lib.load_library()
+    _require_cuda(cache, indices, flags, packed)
+    if indices.dim() != 1 or not indices.is_contiguous():
+        raise KDAError("kda_state_gather", 3, "indices must be a contiguous 1-D tensor")
+    S = indices.shape[0]
+    if packed is None:
+        packed = torch.empty((S,) + tuple(cache.shape[1:]), dtype=cache.dtype, device=cache.device)
+    if packed.dtype != cache.dtype or not packed.is_contiguous() or tuple(packed.shape) != (S,) + tuple(cache.shape[1:]):
+        raise KDAError("kda_state_gather", 3, "packed must be a contiguous [S,H,V,K] tensor of the cache dtype")
+    fptr = None
+    if flags is not None:
+        if flags.dtype not in (torch.bool, torch.uint8) or flags.numel() != S or not flags.is_contiguous():
+            raise KDAError("kda_state_gather", 2, "flags must be a contiguous bool/uint8 tensor of length S")
+        fptr = flags.data_ptr()
+    d = cache_descriptor(cache)
+    st = lib.kda_state_gather(ctypes.byref(d), indices.data_ptr(), _index_code(indices), S, fptr,
+                              packed.data_ptr(), _stream_handle(stream))
+    _lib.check("kda_state_gather", st)
+    return packed
+
+
+def kda_state_scatter(cache: torch.Tensor, indices: torch.Tensor, packed: torch.Tensor, stream=None) -> None:
+    """cache[indices[i]] = packed[i] for every valid index (flags play no part)."""
+    lib = _lib.load_library()
+    _require_cuda(cache, indices, packed)
+    if indices.dim() != 1 or not indices.is_contiguous():
+        raise KDAError("kda_state_scatter", 3, "indices must be a contiguous 1-D tensor")
+    S = indices.shape[0]
+    if packed.dtype != cache.dtype or not packed.is_contiguous() or tuple(packed.shape) != (S,) + tuple(cache.shape[1:]):
+        raise KDAError("kda_state_scatter", 3, "packed must be a contiguous [S,H,V,K] tensor of the cache dtype")
+    d = cache_descriptor(cache)
+    st = lib.kda_state_scatter(ctypes.byref(d), indices.data_ptr(), _index_code(indices), S, packed.data_ptr(),
+                               _stream_handle(stream))
+    _lib.check("kda_state_scatter", st)
+
+
+def kda_chunk_prefill_workspace_size(T: int, N: int, H: int, K: int, V: int) -> int:
+    return int(_lib.load_library().kda_chunk_prefill_workspace_size(T, N, H, K, V))
+
+
+def kda_chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                      cu_seqlens: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+                      final_dtype: Optional[torch.dtype] = torch.float32, scale: Optional[float] = None,
+                      use_qk_l2norm: bool = True, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Chunked gated delta rule over a varlen batch.
+
+    q, k: [T,H,K]; v: [T,H,V] (fp32 or bf16, same dtype); g: [T,H,K] fp32;
+    beta: [T,H]; cu_seqlens: [N+1] int32; initial_state: [N,H,V,K] or None.
+    Returns (out [T,H,V], final_state [N,H,V,K] or None).  ``out`` may be ``v``.
+    ``final_dtype=None`` skips the final state unless ``final_state`` is given.
+    """
+    lib = _lib.load_library()
+    _require_cuda(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, workspace)
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
+        raise KDAError("kda_chunk_prefill", 3, "q,k must be [T,H,K] and v [T,H,V]")
+    T, H, K = (int(x) for x in q.shape)
+    V = int(v.shape[2])
+    N = int(cu_seqlens.numel()) - 1
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("cu_seqlens", cu_seqlens)):
+        if not t.is_contiguous():
+            raise KDAError("kda_chunk_prefill", 4, "%s must be contiguous" % name)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise KDAError("kda_chunk_prefill", 2, "q, k, v must share a dtype")
+    if g.dtype != torch.float32 or tuple(g.shape) != (T, H, K):
+        raise KDAError("kda_chunk_prefill", 2, "g must be float32 [T,H,K]")
+    if tuple(beta.shape) != (T, H):
+        raise KDAError("kda_chunk_prefill", 3, "beta must be [T,H]")
+    if cu_seqlens.dtype != torch.int32 or N < 0:
+        raise KDAError("kda_chunk_prefill", 2, "cu_seqlens must be int32 [N+1]")
+    if out is None:
+        out = torch.empty((T, H, V), dtype=q.dtype, device=q.device)
+    if out.dtype != q.dtype or tuple(out.shape) != (T, H, V) or not out.is_contiguous():
+        raise KDAError("kda_chunk_prefill", 3, "out must be a contiguous [T,H,V] tensor of q's dtype")
+    if final_state is None and final_dtype is not None and N > 0:
+        final_state = torch.empty((N, H, V, K), dtype=final_dtype, device=q.device)
+    for name, s in (("initial_state", initial_state), ("final_state", final_state)):
+        if s is not None and (tuple(s.shape) != (N, H, V, K) or not s.is_contiguous()):
+            raise KDAError("kda_chunk_prefill", 3, "%s must be a contiguous [N,H,V,K] tensor" % name)
+    need = int(lib.kda_chunk_prefill_workspace_size(T, N, H, K, V))
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    a = PrefillArgs()
+    a.T, a.N, a.H, a.K, a.V = T, N, H, K, V
+    a.q, a.k, a.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
+    a.qkv_dtype = _dtype_code(q, "kda_chunk_prefill")
+    a.g = g.data_ptr()
+    a.beta = beta.data_ptr()
+    a.beta_dtype = _dtype_code(beta, "kda_chunk_prefill")
+    a.cu_seqlens = cu_seqlens.data_ptr()
+    a.initial_state = initial_state.data_ptr() if initial_state is not None else None
+    a.initial_dtype = _dtype_code(initial_state, "kda_chunk_prefill") if initial_state is not None else KDA_F32
+    a.out = out.data_ptr()
+    a.final_state = final_state.data_ptr() if final_state is not None else None
+    a.final_dtype = _dtype_code(final_state, "kda_chunk_prefill") if final_state is not None else KDA_F32
+    a.scale = float(K ** -0.5 if scale is None else scale)
+    a.use_qk_l2norm = 1 if use_qk_l2norm else 0
+    a.workspace = workspace.data_ptr() if (workspace is not None and need > 0) else None
+    a.workspace_bytes = need if (workspace is not None and need > 0) else 0
+    st = lib.kda_chunk_prefill(ctypes.byref(a), _stream_handle(stream))
+    _lib.check("kda_chunk_prefill", st)
+    return out, final_state
+
+
+class KDAStateCopy:
+    """A cache view validated once, with a bound on the selection size.
+
+    Mirrors the prepared-plan idea of the vllm-ascend state-copy page (section
+    "启动准备"): the cache layout is checked when the object is made, and a
+    launch that selects more than ``max_selected`` rows is rejected.  Nothing
+    is compiled or retained beyond the tensor reference.
+    """
+
+    def __init__(self, cache: torch.Tensor, max_selected: int):
+        self.cache = cache
+        self.max_selected = int(max_selected)
+        lib = _lib.load_library()
+        d = cache_descriptor(cache)
+        # validate the layout (S = 0 launches nothing)
+        st = lib.kda_state_gather(ctypes.byref(d), None, KDA_I32, 0, None, None, None)
+        _lib.check("KDAStateCopy", st)
+
+    def _check(self, indices: torch.Tensor):
+        if indices.numel() > self.max_selected:
+            raise KDAError("KDAStateCopy", 3, "selected %d rows > max_selected %d"
+                           % (indices.numel(), self.max_selected))
+
+    def gather(self, indices, flags=None, packed=None, stream=None):
+        self._check(indices)
+        return kda_state_gather(self.cache, indices, flags, packed, stream)
+
+    def scatter(self, indices, packed, stream=None):
+        self._check(indices)
+        kda_state_scatter(self.cache, indices, packed, stream)

@@ -218,3 +218,30 @@ def copy_flags(seed, S, n_false):
     fl = np.ones(S, dtype=np.uint8)
     fl[r.permutation(S)[:n_false]] = 0
     return fl
+
+
+def device_cache(num_rows, H, V, K, dtype="bf16", gap=GAP, offset=0, seed=7, std=0.1, device="cuda"):
+    """Like :func:`host_cache` but drawn by torch on ``device`` (for multi-GiB caches).
+
+    Returns (backing, offset, shape, strides) with ``backing`` a 1-D int32
+    (fp32 cache) or int16 (bf16 cache) device tensor of raw bits.
+    """
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    payload = H * V * K
+    stride0 = payload + gap
+    total = offset + (num_rows - 1) * stride0 + payload + gap
+    if dtype == "f32":
+        backing = torch.full((total,), int(SENTINEL_F32.view(np.int32)), dtype=torch.int32, device=device)
+        view = backing.view(torch.float32)
+    else:
+        backing = torch.full((total,), int(SENTINEL_BF16.view(np.int16)), dtype=torch.int16, device=device)
+        view = backing.view(torch.bfloat16)
+    rows = torch.as_strided(view, (num_rows, payload), (stride0, 1), offset)
+    chunk = max(1, (1 << 27) // payload)
+    for r0 in range(0, num_rows, chunk):
+        r1 = min(num_rows, r0 + chunk)
+        vals = torch.randn((r1 - r0, payload), generator=gen, device=device, dtype=torch.float32) * std
+        rows[r0:r1] = vals.to(view.dtype)
+    return backing, offset, (num_rows, H, V, K), (stride0, V * K, K, 1)

@@ -1,0 +1,155 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/kda.h, and its host-side validation rejects bad
+arguments with the documented status before any HIP call is made.  Only
+calls that fail validation, or that validate and enqueue nothing (an empty
+selection, N == 0), are made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from kda_recurrent_state_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from kda_recurrent_state_amd import build
+        build.build()
+    return _lib.load_library()
+
+
+def _declared_functions():
+    with open(os.path.join(ROOT, "include", "kda.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_stages():
+    names = _declared_functions()
+    for n in ("kda_state_gather", "kda_state_scatter", "kda_chunk_prefill"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_python_binding_uses_the_c_names():
+    import kda_recurrent_state_amd as k
+    for n in ("kda_state_gather", "kda_state_scatter", "kda_chunk_prefill", "kda_chunk_prefill_workspace_size"):
+        assert callable(getattr(k, n))
+
+
+def _cache(dtype=0, rows=4, H=2, V=3, K=4, strides=None, data=0x1000):
+    from kda_recurrent_state_amd._lib import StateCache
+    d = StateCache()
+    d.data = data
+    d.dtype = dtype
+    d.num_rows, d.H, d.V, d.K = rows, H, V, K
+    st = strides or (H * V * K + 16, V * K, K, 1)
+    for i in range(4):
+        d.stride[i] = st[i]
+    return d
+
+
+def _gather(lib, d, S=0, idx=None, it=0, packed=None):
+    return lib.kda_state_gather(ctypes.byref(d), idx, it, S, None, packed, None)
+
+
+def test_valid_layout_empty_selection_is_ok(lib):
+    assert _gather(lib, _cache()) == 0
+    assert lib.kda_state_scatter(ctypes.byref(_cache()), None, 1, 0, None, None) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=5), 2),                                   # KDA_E_DTYPE
+    (dict(rows=0), 3),                                    # shape[0] > 0 required
+    (dict(H=0), 3),
+    (dict(strides=(100, 12, 4, 2)), 4),                   # K stride != 1
+    (dict(strides=(100, 12, 5, 1)), 4),                   # V stride != K
+    (dict(strides=(100, 13, 4, 1)), 4),                   # H stride != V*K
+    (dict(strides=(23, 12, 4, 1)), 5),                    # rows overlap (stride0 < payload)
+    (dict(data=0), 1),                                    # NULL base
+])
+def test_layout_rejections(lib, kw, status):
+    assert _gather(lib, _cache(**kw)) == status
+
+
+def test_size_one_dims_may_have_any_stride(lib):
+    # H == 1 and V == 1: their strides are irrelevant to density
+    assert _gather(lib, _cache(H=1, V=1, K=8, strides=(8, 999, 777, 1))) == 0
+    assert _gather(lib, _cache(H=1, V=1, K=8, strides=(8, 999, 777, 2))) == 4
+
+
+def test_gap_is_allowed(lib):
+    assert _gather(lib, _cache(strides=(24 + 4096, 12, 4, 1))) == 0
+
+
+def test_bad_selection_arguments(lib):
+    d = _cache()
+    assert _gather(lib, d, S=-1) == 3
+    assert _gather(lib, d, S=2, idx=None, packed=0x2000) == 1
+    assert _gather(lib, d, S=2, idx=0x3000, packed=None) == 1
+    assert _gather(lib, d, S=0, it=7) == 2
+    assert lib.kda_state_gather(None, None, 0, 0, None, None, None) == 1
+
+
+def _args(**kw):
+    from kda_recurrent_state_amd._lib import PrefillArgs
+    a = PrefillArgs()
+    a.T, a.N, a.H, a.K, a.V = 10, 1, 2, 8, 8
+    a.q, a.k, a.v, a.g, a.beta, a.out = 0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000
+    a.cu_seqlens = 0x7000
+    a.qkv_dtype, a.beta_dtype, a.initial_dtype, a.final_dtype = 1, 0, 0, 0
+    a.scale = 0.35
+    a.use_qk_l2norm = 1
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=0), 3), (dict(V=0), 3), (dict(H=0), 3), (dict(T=-1), 3), (dict(N=-1), 3),
+    (dict(N=0, T=5), 3),
+    (dict(K=129), 6),
+    (dict(qkv_dtype=3), 2), (dict(beta_dtype=9), 2),
+    (dict(cu_seqlens=0), 1), (dict(q=0), 1), (dict(g=0), 1), (dict(out=0), 1),
+    (dict(N=4, workspace=0, workspace_bytes=0), 7),
+    (dict(out=0x3000 + 4), 8),                    # partial overlap with v
+    (dict(out=0x1000), 8),                        # overlaps q
+])
+def test_prefill_rejections(lib, kw, status):
+    a = _args(**kw)
+    assert lib.kda_chunk_prefill(ctypes.byref(a), None) == status
+
+
+def test_prefill_empty_batch_is_ok(lib):
+    a = _args(N=0, T=0)
+    assert lib.kda_chunk_prefill(ctypes.byref(a), None) == 0
+
+
+def test_workspace_size(lib):
+    assert lib.kda_chunk_prefill_workspace_size(100, 1, 32, 128, 128) == 0
+    assert lib.kda_chunk_prefill_workspace_size(100, 200, 32, 128, 128) >= 800
+
+
+def test_status_strings(lib):
+    for s in range(10):
+        assert lib.kda_status_string(s)
+    assert b"KDA_OK" in lib.kda_status_string(0)
+
+
+def test_binding_refuses_without_library(tmp_path):
+    from kda_recurrent_state_amd import _lib
+    saved = _lib._lib
+    try:
+        _lib._lib = None
+        with pytest.raises(ImportError):
+            _lib.load_library(str(tmp_path / "missing.so"))
+    finally:
+        _lib._lib = saved

@@ -1,0 +1,150 @@
+"""GPU parity of kda_chunk_prefill against the fp64 oracle (relative L2 <= 2e-2).
+
+Small cases are compared over every element; they span several chunks and
+tiles, ragged tails, K != V, V-split blocks, zero-length sequences, fp32 and
+bf16 I/O, no initial state, bf16 final states, out aliasing v, strong decays
+that force shorter chunks, split/resume and determinism.
+"""
+import numpy as np
+import pytest
+
+import kda_workloads as wl
+import oracle
+from tests.helpers import REL_TOL, device_inputs, ensure_built, rel_l2, tensor_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    ensure_built()
+
+
+def _run(inp, final_dtype="f32", scale=None, l2norm=True, alias=False, init_override=None):
+    import torch
+    import kda_recurrent_state_amd as kda
+    d = device_inputs(inp)
+    init = d["initial"] if init_override is None else init_override
+    fdt = torch.bfloat16 if final_dtype == "bf16" else torch.float32
+    out = d["v"] if alias else None
+    o, f = kda.kda_chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], initial_state=init,
+                                 out=out, final_dtype=fdt, scale=scale, use_qk_l2norm=l2norm)
+    torch.cuda.synchronize()
+    return tensor_f64(o), tensor_f64(f)
+
+
+def _ref(inp, scale=None, l2norm=True):
+    return oracle.kda_recurrence(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["cu_seqlens"],
+                                 inp["initial"], scale=scale, use_l2norm=l2norm, threads=oracle.default_threads())
+
+
+def _check(inp, **kw):
+    print("case: lengths=%s H=%d K=%d V=%d dtype=%s kw=%s" % (inp["cu_seqlens"].tolist()[:8], inp["H"], inp["K"],
+                                                             inp["V"], inp["dtype"], kw), flush=True)
+    o, f = _run(inp, **{k: v for k, v in kw.items() if k in ("final_dtype", "scale", "l2norm", "alias")})
+    ro, rf = _ref(inp, scale=kw.get("scale"), l2norm=kw.get("l2norm", True))
+    eo, ef = rel_l2(o, ro), rel_l2(f, rf)
+    print("  relL2 out %.3e final %.3e" % (eo, ef), flush=True)
+    assert np.isfinite(o).all() and np.isfinite(f).all()
+    assert eo <= REL_TOL, eo
+    assert ef <= REL_TOL, ef
+    return eo, ef
+
+
+def test_tiny_fp32():
+    inp = wl.host_prefill_inputs(wl.lengths_tiny(), 2, 32, 32, dtype="f32", seed=41)
+    _check(inp)
+
+
+@pytest.mark.parametrize("K,V", [(64, 32), (32, 64), (128, 64), (128, 128), (48, 80), (128, 200)])
+def test_shapes_k_ne_v(K, V):
+    inp = wl.host_prefill_inputs([70, 130], 2, K, V, dtype="bf16", seed=K * 1000 + V)
+    _check(inp)
+
+
+def test_bf16_ragged_varlen():
+    inp = wl.host_prefill_inputs([1, 17, 64, 65, 200, 333, 128], 4, 128, 128, dtype="bf16", seed=5)
+    _check(inp)
+
+
+def test_many_chains_take_full_value_blocks():
+    # N*H >= 512 selects the 128-wide value block
+    inp = wl.host_prefill_inputs([40 + 3 * i for i in range(64)], 8, 128, 128, dtype="bf16", seed=6)
+    _check(inp)
+
+
+def test_zero_length_sequences_pass_state_through():
+    inp = wl.host_prefill_inputs([5, 0, 70, 0], 2, 64, 64, dtype="bf16", seed=7)
+    o, f = _run(inp)
+    ro, rf = _ref(inp)
+    assert rel_l2(o, ro) <= REL_TOL and rel_l2(f, rf) <= REL_TOL
+    assert np.array_equal(f[1], inp["initial"][1]) and np.array_equal(f[3], inp["initial"][3])
+
+
+def test_no_initial_state_and_bf16_final():
+    inp = wl.host_prefill_inputs([100, 300], 2, 128, 128, dtype="bf16", seed=8, initial=False)
+    _check(inp, final_dtype="bf16")
+
+
+def test_scale_one_and_no_l2norm():
+    inp = wl.host_prefill_inputs([90], 2, 64, 64, dtype="f32", seed=9)
+    # unnormalised keys need beta * |k|^2 < 2 for a stable state: shrink k
+    inp["k"] = inp["k"] * np.float32(1.0 / 8.0)
+    _check(inp, scale=1.0, l2norm=False)
+
+
+def test_out_aliases_v():
+    inp = wl.host_prefill_inputs([64, 129], 2, 128, 128, dtype="bf16", seed=10)
+    _check(inp, alias=True)
+
+
+def test_single_token():
+    inp = wl.host_prefill_inputs([1], 1, 128, 128, dtype="bf16", seed=11)
+    _check(inp)
+
+
+@pytest.mark.parametrize("gval", [-30.0, -1e4])
+def test_strong_decay_uses_shorter_chunks(gval):
+    inp = wl.host_prefill_inputs([150, 70], 2, 64, 64, dtype="bf16", seed=12)
+    g = inp["g"].copy()
+    g[::7, :, ::3] = gval          # some channels of some tokens decay (almost) to zero
+    inp["g"] = g
+    _check(inp)
+
+
+def test_no_decay_full_write():
+    inp = wl.host_prefill_inputs([130], 2, 64, 64, dtype="bf16", seed=13)
+    inp["g"] = np.zeros_like(inp["g"])
+    inp["beta"] = np.ones_like(inp["beta"])
+    _check(inp)
+
+
+@pytest.mark.parametrize("split", [64, 100, 1])
+def test_split_and_resume(split):
+    import torch
+    import kda_recurrent_state_amd as kda
+    inp = wl.host_prefill_inputs([256], 2, 128, 128, dtype="bf16", seed=14)
+    d = device_inputs(inp)
+    o_all, f_all = kda.kda_chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"],
+                                         initial_state=d["initial"])
+    cu1 = torch.tensor([0, split], dtype=torch.int32, device="cuda")
+    cu2 = torch.tensor([0, 256 - split], dtype=torch.int32, device="cuda")
+    s = slice(0, split)
+    t = slice(split, 256)
+    o1, f1 = kda.kda_chunk_prefill(d["q"][s].contiguous(), d["k"][s].contiguous(), d["v"][s].contiguous(),
+                                   d["g"][s].contiguous(), d["beta"][s].contiguous(), cu1, initial_state=d["initial"])
+    o2, f2 = kda.kda_chunk_prefill(d["q"][t].contiguous(), d["k"][t].contiguous(), d["v"][t].contiguous(),
+                                   d["g"][t].contiguous(), d["beta"][t].contiguous(), cu2, initial_state=f1)
+    torch.cuda.synchronize()
+    assert rel_l2(tensor_f64(torch.cat([o1, o2])), tensor_f64(o_all)) <= REL_TOL
+    assert rel_l2(tensor_f64(f2), tensor_f64(f_all)) <= REL_TOL
+    ro, rf = _ref(inp)
+    assert rel_l2(tensor_f64(torch.cat([o1, o2])), ro) <= REL_TOL
+    assert rel_l2(tensor_f64(f2), rf) <= REL_TOL
+
+
+def test_deterministic():
+    inp = wl.host_prefill_inputs([300, 77], 4, 128, 128, dtype="bf16", seed=15)
+    o1, f1 = _run(inp)
+    o2, f2 = _run(inp)
+    assert np.array_equal(o1, o2) and np.array_equal(f1, f2)
