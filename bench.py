@@ -1,0 +1,252 @@
+"""Benchmark of the KDA prefill hot path on one MI355X.
+
+One step = one pass of the whole path over one synthetic batch:
+    kda_state_gather -> kda_chunk_prefill -> kda_state_scatter
+on the end-to-end workload: 200 sequences with lengths log-uniform in
+[64, 8192] (about 335k tokens), H=32, K=V=128, bf16 q/k/v, fp32 g and beta,
+and a bf16 state cache [4096,32,128,128] whose rows carry a 4096-element gap
+(address span > 4 GiB); int32 gather indices with duplicates and 10% false
+flags, unique scatter targets.  Inputs are resident in HBM before timing.
+
+Prints ONE JSON line: whole-step tokens/s, per-stage kernel times from HIP
+events on the launch stream, the chunk kernel's HBM roofline fraction, copy
+bandwidths and the oracle timed on the host's cores on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s (H=32,K=V=128) + state gather/scatter GB/s, 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+H, K, V = 32, 128, 128
+NUM_ROWS = 4096
+MAX_SELECTED = 256
+CHUNK_SRC = os.path.join(ROOT, "kda_recurrent_state_amd", "csrc", "chunk_prefill.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_prefill_e2e_traffic.json")
+
+
+def chunk_bytes_per_launch(T: int, N: int) -> int:
+    """Algorithmic HBM bytes of one kda_chunk_prefill launch on this workload.
+
+    Per token-head: q, k, v, o at 2 B x 128 (bf16) = 1024 B, g at 4 B x 128 =
+    512 B, beta 4 B -> 1540 B.  Per (sequence, head): the bf16 initial and
+    final states, 2 x 128 x 128 x 2 B = 64 KiB.  Plus cu_seqlens.
+    """
+    per_tok = 2 * K + 2 * K + 2 * V + 4 * K + 4 + 2 * V
+    return T * H * per_tok + N * H * 2 * (K * V * 2) + 4 * (N + 1)
+
+
+def sha256_file(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def stored_traffic(T: int, N: int):
+    """HBM traffic per launch from committed rocprofv3 counter runs, if they
+    were taken on the current chunk kernel source and this workload."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    if rec.get("chunk_prefill_hip_sha256") != sha256_file(CHUNK_SRC):
+        return None
+    if rec.get("T") != T or rec.get("N") != N:
+        return None
+    return int(rec["hbm_bytes_per_launch"])
+
+
+def build_workload(seed: int, device):
+    import torch
+    import kda_workloads as wl
+
+    lengths = wl.lengths_e2e(seed)
+    inp = wl.device_prefill_inputs(lengths, H, K, V, dtype="bf16", seed=seed, device=device, initial=False)
+    back, off, shape, strides = wl.device_cache(NUM_ROWS, H, V, K, dtype="bf16", gap=wl.GAP, offset=0,
+                                                seed=seed + 1, device=device)
+    cache = torch.as_strided(back.view(torch.bfloat16), shape, strides, off)
+    N = len(lengths)
+    gidx, flags, sidx = wl.e2e_copy_indices(seed, N, NUM_ROWS)
+    packed_in = torch.empty((MAX_SELECTED, H, V, K), dtype=torch.bfloat16, device=device)
+    packed_out = torch.empty((MAX_SELECTED, H, V, K), dtype=torch.bfloat16, device=device)
+    out = torch.empty_like(inp["v"])
+    ws = torch.empty(max(256, 4 * N), dtype=torch.uint8, device=device)
+    return dict(inp=inp, cache=cache, backing=back, N=N, lengths=lengths,
+                gidx=torch.from_numpy(gidx).to(device), flags=torch.from_numpy(flags).to(device),
+                sidx=torch.from_numpy(sidx).to(device), gidx_np=gidx, flags_np=flags, sidx_np=sidx,
+                packed_in=packed_in, packed_out=packed_out, out=out, ws=ws)
+
+
+def cpu_baseline(seed: int, budget_s: float):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import kda_workloads as wl
+    import oracle
+
+    oracle.build(force=False)
+    threads = oracle.default_threads()
+    lengths = wl.lengths_e2e(seed)
+
+    def run(lens):
+        inp = wl.host_prefill_inputs(lens, H, K, V, dtype="bf16", seed=seed + 11, initial=True, init_dtype="bf16")
+        t0 = time.perf_counter()
+        oracle.kda_recurrence(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["cu_seqlens"],
+                              inp["initial"], threads=threads)
+        return time.perf_counter() - t0
+
+    # calibrate on one short sequence, then size the sample to the budget
+    probe = [min(lengths)]
+    t_probe = run(probe)
+    rate = sum(probe) / max(t_probe, 1e-6)
+    target_tokens = max(64, int(rate * budget_s))
+    sample, tot = [], 0
+    for L in lengths:
+        if tot + L > target_tokens and sample:
+            break
+        sample.append(L)
+        tot += L
+    dt = run(sample)
+    return {"value": sum(sample) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "first %d of the %d sequences (%d tokens, all %d heads, K=V=128), fp64 token recurrence, "
+                      "%.1f s" % (len(sample), len(lengths), sum(sample), H, dt)}
+
+
+def calibrate_copy(device, gib: float = 1.0):
+    """A plain device copy of known size, for scaling rocprofv3 byte counters."""
+    import torch
+    n = int(gib * (1 << 30)) // 2
+    src = torch.empty(n, dtype=torch.bfloat16, device=device).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes_read": n * 2, "calibration_copy_bytes_written": n * 2}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--seed", type=int, default=41)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true", help="run only a plain 1 GiB device copy")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this path runs on one GPU; --gpus %d is not supported (sequences and heads shard "
+              "across GPUs with no exchange, see DESIGN.md)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kda_recurrent_state_amd as kda
+    from kda_recurrent_state_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    kda.load_library()
+    dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        calibrate_copy(dev)
+        return
+
+    w = build_workload(args.seed, dev)
+    inp, N = w["inp"], w["N"]
+    T = int(inp["T"])
+    S = N
+    pin, pout = w["packed_in"][:S], w["packed_out"][:S]
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        kda.kda_state_gather(w["cache"], w["gidx"], w["flags"], pin)
+        if ev is not None:
+            ev[1].record(stream)
+        kda.kda_chunk_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["cu_seqlens"],
+                              initial_state=pin, out=w["out"], final_state=pout, workspace=w["ws"])
+        if ev is not None:
+            ev[2].record(stream)
+        kda.kda_state_scatter(w["cache"], w["sidx"], pout)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    g_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    c_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    s_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    ms_per_step = wall * 1e3 / args.steps
+    tokens_per_s = T / (ms_per_step * 1e-3)
+
+    payload = H * V * K * 2
+    flags_np, gidx_np, sidx_np = w["flags_np"], w["gidx_np"], w["sidx_np"]
+    n_read = int(((gidx_np >= 0) & (gidx_np < NUM_ROWS) & (flags_np != 0)).sum())
+    n_valid_s = int(((sidx_np >= 0) & (sidx_np < NUM_ROWS)).sum())
+    gather_bytes = (n_read + S) * payload
+    scatter_bytes = 2 * n_valid_s * payload
+    chunk_bytes = chunk_bytes_per_launch(T, N)
+    c_avg = float(np.mean(c_ms))
+    achieved = chunk_bytes / (c_avg * 1e-3) / 1e9
+    traffic = stored_traffic(T, N)
+    g_avg, s_avg = float(np.mean(g_ms)), float(np.mean(s_ms))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.seed, args.cpu_budget)
+
+    line = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "e2e prefill step: gather -> chunk KDA -> scatter; %d sequences, lengths "
+                               "log-uniform [64,8192], H=32, K=V=128, bf16 q/k/v, fp32 g/beta, bf16 cache "
+                               "[4096,32,128,128] with 4096-element row gap" % N,
+                   "global_batch": N, "seq_len": T, "tokens": T, "parallelism": "none (1 GPU)",
+                   "seed": args.seed},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "kernel": "kda_chunk_prefill", "algorithmic_bytes_per_launch": chunk_bytes,
+                     "avg_launch_ms": c_avg},
+        "cpu_baseline": cpu,
+        "stages_ms": {"gather": g_avg, "chunk_prefill": c_avg, "scatter": s_avg},
+        "copy_GBps": {"gather": gather_bytes / (g_avg * 1e-3) / 1e9,
+                      "scatter": scatter_bytes / (s_avg * 1e-3) / 1e9,
+                      "gather_frac_hbm": gather_bytes / (g_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                      "scatter_frac_hbm": scatter_bytes / (s_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                      "gather_bytes": gather_bytes, "scatter_bytes": scatter_bytes},
+        "chunk_tokens_per_s": T / (c_avg * 1e-3),
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

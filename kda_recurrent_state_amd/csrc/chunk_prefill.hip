@@ -52,50 +52,56 @@
 namespace kda {
 namespace {
 
-constexpr int kC = 64;          // chunk length
-constexpr int kThreads = 256;   // 4 wave64s
+constexpr int kC = 64;  // chunk length
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRangeLimit = 100.f;
 constexpr float kL2Eps = 1e-6f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// KP: key dim padded to 64 or 128.  BV: value columns per workgroup (64 or 128).
+// The workgroup has NW = BV/16 waves; wave w owns value columns [16w, 16w+16)
+// of the block in the state phase and rows [RPW*w, RPW*w + RPW) of the chunk
+// in the elementwise phase.
 template <int KP, int BV>
 struct Cfg {
-  static constexpr int CPL = KP / 64;   // key channels per lane in the elementwise phase
-  static constexpr int VPL = BV / 64;   // value columns per lane in the elementwise phase
-  static constexpr int NVW = BV / 4;    // value columns owned by each wave in the state phase
-  static constexpr int NVT = NVW / 16;  // 16-wide value tiles per wave
-  static constexpr int KT = KP / 16;    // 16-row key tiles
-  static constexpr int KS = KP / 32;    // 32-deep contraction steps over the key dim
-  static constexpr int LDK = KP + 8;    // row stride (bf16) of [64][KP] tiles
-  static constexpr int LDT = kC + 8;    // row stride (bf16) of [X][64] tiles
-  static constexpr int LDA = kC + 4;    // row stride (fp32) of the [64][64] solve tile
-  // LDS map (bytes).  R_KL/R_QL/R_KR are dead after the A products and are
-  // reused for T, -W and the output staging.
+  static constexpr int NW = BV / 16;       // waves
+  static constexpr int NT = NW * 64;       // threads
+  static constexpr int RPW = kC / NW;      // chunk rows per wave, elementwise phase
+  static constexpr int CPL = KP / 64;      // key channels per lane, elementwise phase
+  static constexpr int VPL = BV / 64;      // value columns per lane, elementwise phase
+  static constexpr int KT = KP / 16;       // 16-row key tiles
+  static constexpr int KS = KP / 32;       // 32-deep contraction steps over the key dim
+  static constexpr int LDK = KP + 8;       // row stride (bf16) of [64][KP] tiles
+  static constexpr int LDT = kC + 8;       // row stride (bf16) of [X][64] tiles
+  static constexpr int LDA = kC + 4;       // row stride (fp32) of the [64][64] solve tile
+  static constexpr int LDO = BV + 8;       // row stride (bf16) of the output staging tile
   static constexpr int SZ_ROW = kC * LDK * 2;
   static constexpr int SZ_KT = KP * LDT * 2;
   static constexpr int SZ_VT = BV * LDT * 2;
   static constexpr int SZ_T = kC * LDT * 2;
-  static constexpr int R_KL = 0;                        // KL  [64][KP]  -> T [64][64]
-  static constexpr int R_QL = R_KL + SZ_ROW;            // QL  [64][KP]  -> -W [64][KP]
-  static constexpr int R_KR = R_QL + SZ_ROW;            // KR  [64][KP]
-  static constexpr int R_QG = R_KR + SZ_ROW;            // Qg  [64][KP]
-  static constexpr int R_KE = R_QG + SZ_ROW;            // KE^T [KP][64]
-  static constexpr int R_KB = R_KE + SZ_KT;             // Kbar^T [KP][64]
-  static constexpr int R_VT = R_KB + SZ_KT;             // (beta V)^T [BV][64]
-  static constexpr int R_A = R_VT + SZ_VT;              // A_kk / T fp32 [64][LDA]
-  static constexpr int R_AQK = R_A + kC * LDA * 4;      // A_qk bf16 [64][LDT]
-  static constexpr int R_TOT = R_AQK + SZ_T;            // gate block totals fp32 [4][KP]
-  static constexpr int R_DEC = R_TOT + 4 * KP * 4;      // 2^gamma_L fp32 [KP]
-  static constexpr int R_RED = R_DEC + KP * 4;          // range guard, fp32 [4]
-  static constexpr int R_X = R_RED + 64;                // solve temps fp32 [3 waves][2][16][16]
+  // LDS map (bytes).  KL, QL and KR die after the A products; their space is
+  // reused for T, -W and the output staging tile.
+  static constexpr int R_KL = 0;                    // KL [64][KP]      -> T [64][64]
+  static constexpr int R_QL = R_KL + SZ_ROW;        // QL [64][KP]      -> -W [64][KP]
+  static constexpr int R_KR = R_QL + SZ_ROW;        // KR [64][KP]      -> O staging [64][BV]
+  static constexpr int R_QG = R_KR + SZ_ROW;        // Qg [64][KP]
+  static constexpr int R_KE = R_QG + SZ_ROW;        // KE^T [KP][64]
+  static constexpr int R_KB = R_KE + SZ_KT;         // Kbar^T [KP][64]
+  static constexpr int R_VT = R_KB + SZ_KT;         // (beta V)^T [BV][64]
+  static constexpr int R_A = R_VT + SZ_VT;          // A_kk, then T, fp32 [64][LDA]
+  static constexpr int R_AQK = R_A + kC * LDA * 4;  // A_qk bf16 [64][LDT]
+  static constexpr int R_TOT = R_AQK + SZ_T;        // per-wave gate sums fp32 [NW][KP]
+  static constexpr int R_DEC = R_TOT + NW * KP * 4; // 2^gamma_L fp32 [KP]
+  static constexpr int R_RED = R_DEC + KP * 4;      // range guard fp32 [NW]
+  static constexpr int R_X = R_RED + 64;            // solve temps fp32 [3][2][16][16]
   static constexpr int LDS = R_X + 3 * 2 * 256 * 4;
   static_assert(LDS <= 160 * 1024, "LDS budget");
   static_assert(SZ_T <= SZ_ROW, "T fits in the KL region");
+  static_assert(kC * LDO * 2 <= SZ_ROW, "output staging fits in the KR region");
+  static_assert(RPW == 8 || RPW == 16, "rows per wave");
 };
 
 __device__ __forceinline__ float bf2f(unsigned short u) { return __uint_as_float((unsigned)u << 16); }
@@ -106,20 +112,32 @@ __device__ __forceinline__ float ld_in(const void* p, int64_t i) {
   return static_cast<const float*>(p)[i];
 }
 
-__device__ __forceinline__ float ld_any(const void* p, int64_t i, bool bf16) {
-  return bf16 ? bf2f(static_cast<const unsigned short*>(p)[i]) : static_cast<const float*>(p)[i];
+// Cross-lane reductions: DPP within each 16-lane row (quad swaps, half-row and
+// row mirrors), then the four row results combined through readlane.  Every
+// lane ends with the same bits.
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float lane_f(float x, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
-  return x;
+  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp<0x141>(x);  // row_half_mirror
+  x += dpp<0x140>(x);  // row_mirror
+  return (lane_f(x, 0) + lane_f(x, 16)) + (lane_f(x, 32) + lane_f(x, 48));
 }
 
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
-  return x;
+  x = fmaxf(x, dpp<0xB1>(x));
+  x = fmaxf(x, dpp<0x4E>(x));
+  x = fmaxf(x, dpp<0x141>(x));
+  x = fmaxf(x, dpp<0x140>(x));
+  return fmaxf(fmaxf(lane_f(x, 0), lane_f(x, 16)), fmaxf(lane_f(x, 32), lane_f(x, 48)));
 }
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -127,9 +145,10 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f3
 }
 
 // 8 bf16 from two 4-element runs: k-slots 0..3 <- p[0..3], 4..7 <- p[16..19].
+// Matches the contraction order of pack_perm on two row-adjacent C tiles.
 __device__ __forceinline__ bf16x8 ld_perm(const __bf16* p) {
-  bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
-  bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
+  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
+  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
@@ -137,6 +156,8 @@ __device__ __forceinline__ bf16x8 pack_perm(const f32x4& lo, const f32x4& hi) {
   return bf16x8{(__bf16)lo[0], (__bf16)lo[1], (__bf16)lo[2], (__bf16)lo[3],
                 (__bf16)hi[0], (__bf16)hi[1], (__bf16)hi[2], (__bf16)hi[3]};
 }
+
+__device__ __forceinline__ bf16x8 ld8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
 // Ranks sequences by length, longest first (ties by index).  One workgroup.
 __global__ __launch_bounds__(1024) void plan_order_kernel(const int32_t* __restrict__ cu, int64_t N, int64_t T,
@@ -175,17 +196,23 @@ struct Params {
   int nvb;               // V-blocks per (sequence, head)
   float scale;
   int beta_bf16, init_bf16, fin_bf16, l2norm;
+  int pair;              // K, V even and q/k/v/g 8-byte aligned: two channels per load
+  int ovec;              // V % 8 == 0 and out 16-byte aligned: 16-byte output stores
+  int svec;              // K % 4 == 0 and state pointers aligned: vector state I/O
 };
 
 template <int KP, int BV, bool kBF16>
-__global__ __launch_bounds__(kThreads, 1) void chunk_prefill_kernel(Params p) {
+__global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
   using C = Cfg<KP, BV>;
+  constexpr int NW = C::NW, NT = C::NT, RPW = C::RPW, CPL = C::CPL, VPL = C::VPL;
+  static_assert(NT == BV * 4, "launch bounds");
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
   __bf16* sKL = reinterpret_cast<__bf16*>(smem + C::R_KL);
   __bf16* sT = reinterpret_cast<__bf16*>(smem + C::R_KL);
   __bf16* sQL = reinterpret_cast<__bf16*>(smem + C::R_QL);
   __bf16* sW = reinterpret_cast<__bf16*>(smem + C::R_QL);
   __bf16* sKR = reinterpret_cast<__bf16*>(smem + C::R_KR);
+  __bf16* sO = reinterpret_cast<__bf16*>(smem + C::R_KR);
   __bf16* sQg = reinterpret_cast<__bf16*>(smem + C::R_QG);
   __bf16* sKE = reinterpret_cast<__bf16*>(smem + C::R_KE);
   __bf16* sKB = reinterpret_cast<__bf16*>(smem + C::R_KB);
@@ -198,9 +225,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_prefill_kernel(Params p) {
   float* sX = reinterpret_cast<float*>(smem + C::R_X);
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, provably uniform
   const int l = tid & 63;
-  const int lr = l & 15;  // MFMA row/col within a 16-tile
+  const int lr = l & 15;  // MFMA row (A) / column (B, C) within a 16-tile
   const int lg = l >> 4;  // MFMA k-group
 
   // ---- work item: XCD-aware mapping, V-block siblings share blockIdx % 8 ----
@@ -219,80 +246,182 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_prefill_kernel(Params p) {
   bos = bos < 0 ? 0 : (bos > p.T ? p.T : bos);
   eos = eos < bos ? bos : (eos > p.T ? p.T : eos);
   const int64_t len = eos - bos;
-  const int64_t v0 = (int64_t)vb * BV;  // first value column of this block
+  const int64_t v0 = (int64_t)vb * BV;   // first value column of this block
+  const int64_t vcol = v0 + 16 * w + lr; // this lane's state column (state phase)
+  const int64_t vcl = vcol < V ? vcol : V - 1;
+  const int64_t srow = (n * H + h) * V;  // state row base of (n, h), in units of K elements
 
   // A_qk upper blocks are read by the output product but never written: zero once.
-  for (int e = tid; e < kC * kC; e += kThreads) {
+  for (int e = tid; e < kC * kC; e += NT) {
     const int r = e >> 6, c = e & 63;
     if ((c >> 4) > (r >> 4)) sAqk[r * C::LDT + c] = (__bf16)0.f;
   }
 
-  // ---- initial state into MFMA C-layout registers ----
-  // S[ct][vt][e] = S(c = 16ct + 4lg + e, v = v0 + w*NVW + 16vt + lr)
-  f32x4 S[C::KT][C::NVT];
+  // ---- initial state, MFMA C layout: S[ct][e] = S(c = 16ct + 4lg + e, vcol) ----
+  f32x4 S[C::KT];
+  if (p.init) {
+    if (p.svec) {
 #pragma unroll
-  for (int ct = 0; ct < C::KT; ++ct)
-#pragma unroll
-    for (int vt = 0; vt < C::NVT; ++vt) {
-      const int64_t vcol = v0 + w * C::NVW + 16 * vt + lr;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t c = 16 * ct + 4 * lg + e;
-        float x = 0.f;
-        if (p.init && vcol < V && c < K) x = ld_any(p.init, ((n * H + h) * V + vcol) * K + c, p.init_bf16);
-        S[ct][vt][e] = x;
+      for (int ct = 0; ct < C::KT; ++ct) {
+        const int64_t c0 = 16 * ct + 4 * lg;
+        const int64_t cs = c0 < K ? c0 : K - 4;
+        const int64_t o = (srow + vcl) * K + cs;
+        if (p.init_bf16) {
+          const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const unsigned short*>(p.init) + o);
+          S[ct] = f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                        __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+        } else {
+          S[ct] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.init) + o);
+        }
       }
+    } else {
+#pragma unroll
+      for (int ct = 0; ct < C::KT; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t c = 16 * ct + 4 * lg + e;
+          const int64_t o = (srow + vcl) * K + (c < K ? c : K - 1);
+          S[ct][e] = p.init_bf16 ? bf2f(static_cast<const unsigned short*>(p.init)[o])
+                                 : static_cast<const float*>(p.init)[o];
+        }
     }
+#pragma unroll
+    for (int ct = 0; ct < C::KT; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[ct][e] = (vcol < V && 16 * ct + 4 * lg + e < K) ? S[ct][e] : 0.f;
+  } else {
+#pragma unroll
+    for (int ct = 0; ct < C::KT; ++ct) S[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   const float scale = p.scale;
+  const int64_t c_lo = (int64_t)l * CPL;       // first key channel of this lane (elementwise phase)
+  const int64_t vc_lo = v0 + (int64_t)l * VPL; // first value column of this lane (elementwise phase)
   int64_t t0 = 0;
   int Lcap = kC;
   while (t0 < len) {
-    int L = (int)((len - t0) < (int64_t)Lcap ? (len - t0) : (int64_t)Lcap);
-    __syncthreads();  // previous chunk's readers of LDS are done
+    const int L = (int)((len - t0) < (int64_t)Lcap ? (len - t0) : (int64_t)Lcap);
+    __syncthreads();  // the previous chunk's LDS readers are done
 
-    // ---------------- phase 0: loads, l2norm, gate cumsum -----------------
-    float kx[16][C::CPL], qx[16][C::CPL], gx[16][C::CPL], vx[16][C::VPL], bt[16];
+    // ---------------- phase 0: loads, (beta V)^T, gate sums, norms ----------
+    // All loads are unconditional (row clamped to the last valid row, channel
+    // to the last valid channel) so they are in flight together; values
+    // outside the chunk or the key/value range are zeroed afterwards.
+    float kx[RPW][CPL], qx[RPW][CPL], gx[RPW][CPL], vx[RPW][VPL], bt[RPW];
+    int64_t th[RPW];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = 16 * w + r;
-      const bool ok = i < L;
-      const int64_t t = bos + t0 + i;
-      const int64_t bk = (t * H + h) * K;
-#pragma unroll
-      for (int cc = 0; cc < C::CPL; ++cc) {
-        const int64_t c = l * C::CPL + cc;
-        const bool okc = ok && c < K;
-        kx[r][cc] = okc ? ld_in<kBF16>(p.k, bk + c) : 0.f;
-        qx[r][cc] = okc ? ld_in<kBF16>(p.q, bk + c) : 0.f;
-        gx[r][cc] = okc ? p.g[bk + c] : 0.f;
-      }
-      const int64_t bv = (t * H + h) * V + v0;
-#pragma unroll
-      for (int vv = 0; vv < C::VPL; ++vv) {
-        const int64_t vc = l * C::VPL + vv;
-        vx[r][vv] = (ok && v0 + vc < V) ? ld_in<kBF16>(p.v, bv + vc) : 0.f;
-      }
-      bt[r] = ok ? ld_any(p.beta, t * H + h, p.beta_bf16) : 0.f;
+    for (int r = 0; r < RPW; ++r) {
+      const int i = RPW * w + r;
+      th[r] = (bos + t0 + (i < L ? i : L - 1)) * H + h;
     }
-    // inclusive cumsum of g over this wave's 16 rows
+    if (p.beta_bf16) {
 #pragma unroll
-    for (int cc = 0; cc < C::CPL; ++cc) {
+      for (int r = 0; r < RPW; ++r) bt[r] = bf2f(static_cast<const unsigned short*>(p.beta)[th[r]]);
+    } else {
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) bt[r] = static_cast<const float*>(p.beta)[th[r]];
+    }
+    if (CPL == 2 && p.pair) {
+      const int64_t cs = c_lo + 1 < K ? c_lo : K - 2;
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        if (kBF16) {
+          const unsigned wk = *reinterpret_cast<const unsigned*>(static_cast<const unsigned short*>(p.k) + th[r] * K + cs);
+          const unsigned wq = *reinterpret_cast<const unsigned*>(static_cast<const unsigned short*>(p.q) + th[r] * K + cs);
+          kx[r][0] = __uint_as_float(wk << 16);
+          kx[r][CPL - 1] = __uint_as_float(wk & 0xffff0000u);
+          qx[r][0] = __uint_as_float(wq << 16);
+          qx[r][CPL - 1] = __uint_as_float(wq & 0xffff0000u);
+        } else {
+          const float2 fk = *reinterpret_cast<const float2*>(static_cast<const float*>(p.k) + th[r] * K + cs);
+          const float2 fq = *reinterpret_cast<const float2*>(static_cast<const float*>(p.q) + th[r] * K + cs);
+          kx[r][0] = fk.x;
+          kx[r][CPL - 1] = fk.y;
+          qx[r][0] = fq.x;
+          qx[r][CPL - 1] = fq.y;
+        }
+        const float2 fg = *reinterpret_cast<const float2*>(p.g + th[r] * K + cs);
+        gx[r][0] = fg.x;
+        gx[r][CPL - 1] = fg.y;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < RPW; ++r)
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+          const int64_t cs = c_lo + cc < K ? c_lo + cc : K - 1;
+          kx[r][cc] = ld_in<kBF16>(p.k, th[r] * K + cs);
+          qx[r][cc] = ld_in<kBF16>(p.q, th[r] * K + cs);
+          gx[r][cc] = p.g[th[r] * K + cs];
+        }
+    }
+    if (VPL == 2 && p.pair) {
+      const int64_t vs = vc_lo + 1 < V ? vc_lo : V - 2;
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        if (kBF16) {
+          const unsigned wv = *reinterpret_cast<const unsigned*>(static_cast<const unsigned short*>(p.v) + th[r] * V + vs);
+          vx[r][0] = __uint_as_float(wv << 16);
+          vx[r][VPL - 1] = __uint_as_float(wv & 0xffff0000u);
+        } else {
+          const float2 fv = *reinterpret_cast<const float2*>(static_cast<const float*>(p.v) + th[r] * V + vs);
+          vx[r][0] = fv.x;
+          vx[r][VPL - 1] = fv.y;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < RPW; ++r)
+#pragma unroll
+        for (int vv = 0; vv < VPL; ++vv) {
+          const int64_t vs = vc_lo + vv < V ? vc_lo + vv : V - 1;
+          vx[r][vv] = ld_in<kBF16>(p.v, th[r] * V + vs);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const bool okr = RPW * w + r < L;
+      bt[r] = okr ? bt[r] : 0.f;
+#pragma unroll
+      for (int cc = 0; cc < CPL; ++cc) {
+        const bool okc = okr && c_lo + cc < K;
+        kx[r][cc] = okc ? kx[r][cc] : 0.f;
+        qx[r][cc] = okc ? qx[r][cc] : 0.f;
+        gx[r][cc] = okc ? gx[r][cc] : 0.f;
+      }
+#pragma unroll
+      for (int vv = 0; vv < VPL; ++vv) vx[r][vv] = (okr && vc_lo + vv < V) ? vx[r][vv] : 0.f;
+    }
+    // (beta V)^T: this lane's RPW consecutive rows of each of its value columns
+#pragma unroll
+    for (int vv = 0; vv < VPL; ++vv) {
+      bf16x8* pv = reinterpret_cast<bf16x8*>(sVT + (l * VPL + vv) * C::LDT + RPW * w);
+#pragma unroll
+      for (int h8 = 0; h8 < RPW / 8; ++h8) {
+        bf16x8 x;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = (__bf16)(bt[8 * h8 + j] * vx[8 * h8 + j][vv]);
+        pv[h8] = x;
+      }
+    }
+    // inclusive sum of g over this wave's rows
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc) {
       float run = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
+      for (int r = 0; r < RPW; ++r) {
         run += gx[r][cc];
         gx[r][cc] = run;
       }
-      sTot[w * KP + l * C::CPL + cc] = run;
+      sTot[w * KP + c_lo + cc] = run;
     }
-    // row norms
-    float rk[16], rq[16];
+    // 1 / |row| for q and k
+    float rk[RPW], rq[RPW];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < RPW; ++r) {
       float sk = 0.f, sq = 0.f;
 #pragma unroll
-      for (int cc = 0; cc < C::CPL; ++cc) {
+      for (int cc = 0; cc < CPL; ++cc) {
         sk += kx[r][cc] * kx[r][cc];
         sq += qx[r][cc] * qx[r][cc];
       }
@@ -303,25 +432,25 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_prefill_kernel(Params p) {
     }
     __syncthreads();
 
-    // gamma (log2 units), reference row and range guard
-    const int mb = L > 32 ? 2 : 1;  // reference = last row of block mb-1
-    float gm[C::CPL], gL[C::CPL];
+    // gamma in log2 units, the reference row m and the range guard
+    const int mw = (L > 32 ? 32 : 16) / RPW;  // waves whose rows precede the reference boundary
+    float gm[CPL], gL[CPL];
     float guard = 0.f;
 #pragma unroll
-    for (int cc = 0; cc < C::CPL; ++cc) {
-      const int c = l * C::CPL + cc;
+    for (int cc = 0; cc < CPL; ++cc) {
+      const int64_t c = c_lo + cc;
       float off = 0.f, ref = 0.f, tot = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < 4; ++ww) {
+      for (int ww = 0; ww < NW; ++ww) {
         const float x = sTot[ww * KP + c];
         off += ww < w ? x : 0.f;
-        ref += ww < mb ? x : 0.f;
+        ref += ww < mw ? x : 0.f;
         tot += x;
       }
       gm[cc] = ref * kLog2e;
       gL[cc] = tot * kLog2e;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
+      for (int r = 0; r < RPW; ++r) {
         gx[r][cc] = (gx[r][cc] + off) * kLog2e;
         guard = fmaxf(guard, fabsf(gx[r][cc] - gm[cc]));
       }
@@ -330,7 +459,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_prefill_kernel(Params p) {
     guard = wave_max(guard);
     if (l == 0) sRed[w] = guard;
     __syncthreads();
-    const float gmax = fmaxf(fmaxf(sRed[0], sRed[1]), fmaxf(sRed[2], sRed[3]));
+    float gmax = sRed[0];
+#pragma unroll
+    for (int ww = 1; ww < NW; ++ww) gmax = fmaxf(gmax, sRed[ww]);
     if (gmax > kRangeLimit && L > 1) {
       Lcap = L > 16 ? 16 : (L > 4 ? 4 : 1);
       continue;  // re-process this span as shorter chunks
@@ -338,15 +469,15 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_prefill_kernel(Params p) {
 
     // ---------------- phase A: gated operand tiles into LDS ----------------
 #pragma unroll
-    for (int cc = 0; cc < C::CPL; ++cc) {
-      const int c = l * C::CPL + cc;
+    for (int cc = 0; cc < CPL; ++cc) {
+      const int64_t c = c_lo + cc;
       const float cg = __builtin_amdgcn_exp2f(gm[cc]);           // 2^gamma_m
       const float cb = __builtin_amdgcn_exp2f(gL[cc] - gm[cc]);  // 2^(gamma_L - gamma_m)
       if (w == 0) sDec[c] = __builtin_amdgcn_exp2f(gL[cc]);
-      __bf16 ke[16], kb[16];
+      __bf16 ke[RPW], kb[RPW];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = 16 * w + r;
+      for (int r = 0; r < RPW; ++r) {
+        const int i = RPW * w + r;
         const float e1 = __builtin_amdgcn_exp2f(gx[r][cc] - gm[cc]);  // 2^(gamma_i - gamma_m)
         const float e2 = __builtin_amdgcn_exp2f(gm[cc] - gx[r][cc]);  // 2^(gamma_m - gamma_i)
         const float kh = kx[r][cc] * rk[r];
@@ -358,42 +489,36 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_prefill_kernel(Params p) {
         ke[r] = (__bf16)(bt[r] * kh * (e1 * cg));
         kb[r] = (__bf16)(kh * (e2 * cb));
       }
-      // transposed tiles: 16 consecutive rows of one channel = two 16-byte stores
-      bf16x8* pe = reinterpret_cast<bf16x8*>(sKE + c * C::LDT + 16 * w);
-      bf16x8* pb = reinterpret_cast<bf16x8*>(sKB + c * C::LDT + 16 * w);
-      pe[0] = bf16x8{ke[0], ke[1], ke[2], ke[3], ke[4], ke[5], ke[6], ke[7]};
-      pe[1] = bf16x8{ke[8], ke[9], ke[10], ke[11], ke[12], ke[13], ke[14], ke[15]};
-      pb[0] = bf16x8{kb[0], kb[1], kb[2], kb[3], kb[4], kb[5], kb[6], kb[7]};
-      pb[1] = bf16x8{kb[8], kb[9], kb[10], kb[11], kb[12], kb[13], kb[14], kb[15]};
-    }
+      // transposed tiles: RPW consecutive rows of one channel, 16-byte stores
+      bf16x8* pe = reinterpret_cast<bf16x8*>(sKE + c * C::LDT + RPW * w);
+      bf16x8* pb = reinterpret_cast<bf16x8*>(sKB + c * C::LDT + RPW * w);
 #pragma unroll
-    for (int vv = 0; vv < C::VPL; ++vv) {
-      const int vc = l * C::VPL + vv;
-      __bf16 bvv[16];
+      for (int h8 = 0; h8 < RPW / 8; ++h8) {
+        bf16x8 xe, xb;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) bvv[r] = (__bf16)(bt[r] * vx[r][vv]);
-      bf16x8* pv = reinterpret_cast<bf16x8*>(sVT + vc * C::LDT + 16 * w);
-      pv[0] = bf16x8{bvv[0], bvv[1], bvv[2], bvv[3], bvv[4], bvv[5], bvv[6], bvv[7]};
-      pv[1] = bf16x8{bvv[8], bvv[9], bvv[10], bvv[11], bvv[12], bvv[13], bvv[14], bvv[15]};
+        for (int j = 0; j < 8; ++j) {
+          xe[j] = ke[8 * h8 + j];
+          xb[j] = kb[8 * h8 + j];
+        }
+        pe[h8] = xe;
+        pb[h8] = xb;
+      }
     }
     __syncthreads();
 
     // ---------------- phase B: A_kk (fp32) and A_qk (bf16) -----------------
-    // 10 lower block pairs x {kk, qk} = 20 tile jobs, round-robin over waves.
-    for (int job = w; job < 20; job += 4) {
+    // 10 lower 16x16 block pairs x {kk, qk} = 20 tile jobs, round-robin over waves.
+    for (int job = w; job < 20; job += NW) {
       const int pair = job >> 1;
       const bool is_qk = job & 1;
-      // pair -> (bi, bj), bj <= bi
       const int bi = pair >= 6 ? 3 : (pair >= 3 ? 2 : (pair >= 1 ? 1 : 0));
       const int bj = pair - (bi * (bi + 1)) / 2;
       const __bf16* left = is_qk ? sQL : sKL;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(left + (16 * bi + lr) * C::LDK + 32 * ks + 8 * lg);
-        const bf16x8 bb = *reinterpret_cast<const bf16x8*>(sKR + (16 * bj + lr) * C::LDK + 32 * ks + 8 * lg);
-        acc = mfma(a, bb, acc);
-      }
+      for (int ks = 0; ks < C::KS; ++ks)
+        acc = mfma(ld8(left + (16 * bi + lr) * C::LDK + 32 * ks + 8 * lg),
+                   ld8(sKR + (16 * bj + lr) * C::LDK + 32 * ks + 8 * lg), acc);
       const int col = 16 * bj + lr;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -408,20 +533,23 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_prefill_kernel(Params p) {
 
     // ---------------- phase C: T = (I + A_kk)^-1, in place in sA ----------
     if (w == 0) {
-      // diagonal 16x16 blocks by forward substitution; lane = (block, column)
-      const int bb = l >> 4, col = l & 15;
-      const float* Ab = sA + (16 * bb) * C::LDA + 16 * bb;
+      // diagonal 16x16 blocks by substitution; lane = (block, column)
+      const int bb = l >> 4;
+      int col = l & 15;
+      asm volatile("" : "+v"(col));  // keep the identity column below from being hoisted out of the chunk loop
+      float* Ab = sA + (16 * bb) * C::LDA + 16 * bb;
       float x[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float s = (i == col) ? 1.f : 0.f;
+      for (int i = 0; i < 16; ++i) x[i] = (i == col) ? 1.f : 0.f;
 #pragma unroll
-        for (int j = 0; j < i; ++j) s -= Ab[i * C::LDA + j] * x[j];
-        x[i] = s;
+      for (int j = 0; j < 15; ++j) {
+#pragma unroll
+        for (int i = j + 1; i < 16; ++i) x[i] -= Ab[i * C::LDA + j] * x[j];
+        // bound how many triangle reads the scheduler hoists (register pressure)
+        if (j % 4 == 3) __builtin_amdgcn_sched_barrier(0);
       }
-      float* Tb = sA + (16 * bb) * C::LDA + 16 * bb;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) Tb[i * C::LDA + col] = x[i];
+      for (int i = 0; i < 16; ++i) Ab[i * C::LDA + col] = x[i];
     }
     __syncthreads();
     // off-diagonal blocks, one block row at a time:
@@ -442,7 +570,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_prefill_kernel(Params p) {
           }
         }
         *reinterpret_cast<f32x4*>(X + r * 16 + c0) = xs;
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): X visible to the wave
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): X visible to the whole wave
         __builtin_amdgcn_wave_barrier();
         f32x4 ys = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -455,49 +583,30 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_prefill_kernel(Params p) {
       }
       __syncthreads();
       if (w < bi) {
-        const int bj = w;
         const int r = l >> 2, c0 = 4 * (l & 3);
-        const float* Y = sX + w * 512 + 256;
-        *reinterpret_cast<f32x4*>(sA + (16 * bi + r) * C::LDA + 16 * bj + c0) =
-            *reinterpret_cast<const f32x4*>(Y + r * 16 + c0);
+        *reinterpret_cast<f32x4*>(sA + (16 * bi + r) * C::LDA + 16 * w + c0) =
+            *reinterpret_cast<const f32x4*>(sX + w * 512 + 256 + r * 16 + c0);
       }
       __syncthreads();
     }
-    // T to bf16 [64][LDT] with zeros above the diagonal (overwrites KL)
-    for (int e = tid; e < kC * kC; e += kThreads) {
+    // T to bf16 [64][LDT] with zeros above the diagonal (KL is dead)
+    for (int e = tid; e < kC * kC; e += NT) {
       const int r = e >> 6, c = e & 63;
       sT[r * C::LDT + c] = (__bf16)(c <= r ? sA[r * C::LDA + c] : 0.f);
     }
     __syncthreads();
 
-    // ---------------- phase D: U (registers) and -W (LDS) ------------------
-    f32x4 U[4][C::NVT];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int vt = 0; vt < C::NVT; ++vt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          if (32 * ks > 16 * rt + 15) continue;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sT + (16 * rt + lr) * C::LDT + 32 * ks + 8 * lg);
-          const bf16x8 bb =
-              *reinterpret_cast<const bf16x8*>(sVT + (w * C::NVW + 16 * vt + lr) * C::LDT + 32 * ks + 8 * lg);
-          acc = mfma(a, bb, acc);
-        }
-        U[rt][vt] = acc;
-      }
-    // W^T[c][i] = sum_j KE^T[c][j] T[i][j]; stored as -W[i][c]
-    for (int ct = w; ct < C::KT; ct += 4) {
+    // ---------------- phase D: -W into LDS (QL is dead) --------------------
+    // W^T[c][i] = sum_j KE^T[c][j] T[i][j]
+    for (int ct = w; ct < C::KT; ct += NW) {
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           if (32 * ks > 16 * it + 15) continue;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sKE + (16 * ct + lr) * C::LDT + 32 * ks + 8 * lg);
-          const bf16x8 bb = *reinterpret_cast<const bf16x8*>(sT + (16 * it + lr) * C::LDT + 32 * ks + 8 * lg);
-          acc = mfma(a, bb, acc);
+          acc = mfma(ld8(sKE + (16 * ct + lr) * C::LDT + 32 * ks + 8 * lg),
+                     ld8(sT + (16 * it + lr) * C::LDT + 32 * ks + 8 * lg), acc);
         }
         *reinterpret_cast<bf16x4*>(sW + (16 * it + lr) * C::LDK + 16 * ct + 4 * lg) =
             bf16x4{(__bf16)(-acc[0]), (__bf16)(-acc[1]), (__bf16)(-acc[2]), (__bf16)(-acc[3])};
@@ -505,105 +614,115 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_prefill_kernel(Params p) {
     }
     __syncthreads();
 
-    // ---------------- phase E: the serial chain, per wave ------------------
-    bf16x8 bS[C::KS][C::NVT];
+    // ---------------- phase E: the serial chain on this wave's 16 columns ----
+    // U = T (beta V), V_new = U - W S, O = Qg S + A_qk V_new, S = D S + Kbar^T V_new
+    bf16x8 bS[C::KS];
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-      for (int vt = 0; vt < C::NVT; ++vt) bS[ks][vt] = pack_perm(S[2 * ks][vt], S[2 * ks + 1][vt]);
-    // V_new = U - W S
-    f32x4 Vn[4][C::NVT];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int vt = 0; vt < C::NVT; ++vt) Vn[rt][vt] = U[rt][vt];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8 a = ld_perm(sW + (16 * rt + lr) * C::LDK + 32 * ks + 4 * lg);
-#pragma unroll
-        for (int vt = 0; vt < C::NVT; ++vt) Vn[rt][vt] = mfma(a, bS[ks][vt], Vn[rt][vt]);
-      }
-    bf16x8 bV[2][C::NVT];
-#pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2)
-#pragma unroll
-      for (int vt = 0; vt < C::NVT; ++vt) bV[q2][vt] = pack_perm(Vn[2 * q2][vt], Vn[2 * q2 + 1][vt]);
-    // O = Qg S_in + A_qk V_new
-    f32x4 O[4][C::NVT];
+    for (int ks = 0; ks < C::KS; ++ks) bS[ks] = pack_perm(S[2 * ks], S[2 * ks + 1]);
+    f32x4 Vn[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int vt = 0; vt < C::NVT; ++vt) O[rt][vt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8 a = ld_perm(sQg + (16 * rt + lr) * C::LDK + 32 * ks + 4 * lg);
-#pragma unroll
-        for (int vt = 0; vt < C::NVT; ++vt) O[rt][vt] = mfma(a, bS[ks][vt], O[rt][vt]);
+      for (int ks = 0; ks < 2; ++ks) {
+        if (32 * ks > 16 * rt + 15) continue;
+        acc = mfma(ld8(sT + (16 * rt + lr) * C::LDT + 32 * ks + 8 * lg),
+                   ld8(sVT + (16 * w + lr) * C::LDT + 32 * ks + 8 * lg), acc);
       }
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) acc = mfma(ld_perm(sW + (16 * rt + lr) * C::LDK + 32 * ks + 4 * lg), bS[ks], acc);
+      Vn[rt] = acc;
+    }
+    bf16x8 bV[2];
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) bV[q2] = pack_perm(Vn[2 * q2], Vn[2 * q2 + 1]);
+    f32x4 O[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) acc = mfma(ld_perm(sQg + (16 * rt + lr) * C::LDK + 32 * ks + 4 * lg), bS[ks], acc);
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2) {
         if (32 * q2 > 16 * rt + 15) continue;
-        const bf16x8 a = ld_perm(sAqk + (16 * rt + lr) * C::LDT + 32 * q2 + 4 * lg);
-#pragma unroll
-        for (int vt = 0; vt < C::NVT; ++vt) O[rt][vt] = mfma(a, bV[q2][vt], O[rt][vt]);
+        acc = mfma(ld_perm(sAqk + (16 * rt + lr) * C::LDT + 32 * q2 + 4 * lg), bV[q2], acc);
       }
+      O[rt] = acc;
     }
-    // S = diag(2^gamma_L) S + Kbar^T V_new
 #pragma unroll
     for (int ct = 0; ct < C::KT; ++ct) {
       const f32x4 dec = *reinterpret_cast<const f32x4*>(sDec + 16 * ct + 4 * lg);
+      f32x4 acc = S[ct] * dec;
 #pragma unroll
-      for (int vt = 0; vt < C::NVT; ++vt) S[ct][vt] *= dec;
-#pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
-        const bf16x8 a = ld_perm(sKB + (16 * ct + lr) * C::LDT + 32 * q2 + 4 * lg);
-#pragma unroll
-        for (int vt = 0; vt < C::NVT; ++vt) S[ct][vt] = mfma(a, bV[q2][vt], S[ct][vt]);
-      }
+      for (int q2 = 0; q2 < 2; ++q2) acc = mfma(ld_perm(sKB + (16 * ct + lr) * C::LDT + 32 * q2 + 4 * lg), bV[q2], acc);
+      S[ct] = acc;
     }
-    // output rows of this chunk
+
+    // ---------------- output rows of this chunk ---------------------------
+    if (kBF16 && p.ovec) {
+      // stage through LDS (KR is dead) and store whole 16-byte runs of rows
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+      for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int vt = 0; vt < C::NVT; ++vt) {
-        const int64_t vcol = v0 + w * C::NVW + 16 * vt + lr;
-        if (vcol >= V) continue;
+        for (int e = 0; e < 4; ++e) sO[(16 * rt + 4 * lg + e) * C::LDO + 16 * w + lr] = (__bf16)O[rt][e];
+      __syncthreads();
+      constexpr int VPR = BV / 8;  // 16-byte runs per row
+#pragma unroll
+      for (int u0 = 0; u0 < kC * VPR; u0 += NT) {
+        const int u = u0 + tid;
+        const int i = u / VPR, cv = u - i * VPR;
+        if (i < L && v0 + 8 * cv < V) {
+          const int64_t o = ((bos + t0 + i) * H + h) * V + v0 + 8 * cv;
+          *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(p.out) + o) = ld8(sO + i * C::LDO + 8 * cv);
+        }
+      }
+    } else if (vcol < V) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 16 * rt + 4 * lg + e;
-          if (i >= L) continue;
-          const int64_t o = ((bos + t0 + i) * H + h) * V + vcol;
-          if (kBF16)
-            static_cast<__bf16*>(p.out)[o] = (__bf16)O[rt][vt][e];
-          else
-            static_cast<float*>(p.out)[o] = O[rt][vt][e];
+          if (i < L) {
+            const int64_t o = ((bos + t0 + i) * H + h) * V + vcol;
+            if (kBF16)
+              static_cast<__bf16*>(p.out)[o] = (__bf16)O[rt][e];
+            else
+              static_cast<float*>(p.out)[o] = O[rt][e];
+          }
         }
-      }
+    }
     t0 += L;
     Lcap = kC;
   }
 
   // ---- final state ----
-  if (p.fin) {
+  if (p.fin && vcol < V) {
+    if (p.svec) {
 #pragma unroll
-    for (int ct = 0; ct < C::KT; ++ct)
+      for (int ct = 0; ct < C::KT; ++ct) {
+        const int64_t c0 = 16 * ct + 4 * lg;
+        if (c0 >= K) continue;
+        const int64_t o = (srow + vcol) * K + c0;
+        if (p.fin_bf16)
+          *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(p.fin) + o) =
+              bf16x4{(__bf16)S[ct][0], (__bf16)S[ct][1], (__bf16)S[ct][2], (__bf16)S[ct][3]};
+        else
+          *reinterpret_cast<f32x4*>(static_cast<float*>(p.fin) + o) = S[ct];
+      }
+    } else {
 #pragma unroll
-      for (int vt = 0; vt < C::NVT; ++vt) {
-        const int64_t vcol = v0 + w * C::NVW + 16 * vt + lr;
-        if (vcol >= V) continue;
+      for (int ct = 0; ct < C::KT; ++ct)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int64_t c = 16 * ct + 4 * lg + e;
           if (c >= K) continue;
-          const int64_t o = ((n * H + h) * V + vcol) * K + c;
+          const int64_t o = (srow + vcol) * K + c;
           if (p.fin_bf16)
-            static_cast<__bf16*>(p.fin)[o] = (__bf16)S[ct][vt][e];
+            static_cast<__bf16*>(p.fin)[o] = (__bf16)S[ct][e];
           else
-            static_cast<float*>(p.fin)[o] = S[ct][vt][e];
+            static_cast<float*>(p.fin)[o] = S[ct][e];
         }
-      }
+    }
   }
 }
 
@@ -614,32 +733,52 @@ hipError_t launch_cfg(const Params& prm, bool bf16, hipStream_t stream) {
   const int64_t items = prm.N * prm.H;
   const int64_t groups = (items + 7) / 8;
   const int64_t grid = groups * 8 * prm.nvb;
+  constexpr int nt = Cfg<KP, BV>::NT;
   if (bf16)
-    hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, prm);
+    hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, true>), dim3((unsigned)grid), dim3(nt), 0, stream, prm);
   else
-    hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, prm);
+    hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, false>), dim3((unsigned)grid), dim3(nt), 0, stream, prm);
   return hipGetLastError();
 }
 
 }  // namespace
 
 size_t chunk_prefill_workspace_bytes(int64_t T, int64_t N, int64_t H, int64_t K, int64_t V) {
-  (void)T; (void)H; (void)K; (void)V;
+  (void)T;
+  (void)H;
+  (void)K;
+  (void)V;
   if (N < 2 || N > kPlanMaxN) return 0;
   return (size_t)(((N * 4) + 255) / 256 * 256);
 }
 
 hipError_t launch_chunk_prefill(const kda_prefill_args_t& a, hipStream_t stream) {
   Params prm;
-  prm.q = a.q; prm.k = a.k; prm.v = a.v; prm.g = a.g; prm.beta = a.beta; prm.cu = a.cu_seqlens;
-  prm.init = a.initial_state; prm.out = a.out; prm.fin = a.final_state;
-  prm.T = a.T; prm.N = a.N; prm.H = a.H; prm.K = a.K; prm.V = a.V;
+  prm.q = a.q;
+  prm.k = a.k;
+  prm.v = a.v;
+  prm.g = a.g;
+  prm.beta = a.beta;
+  prm.cu = a.cu_seqlens;
+  prm.init = a.initial_state;
+  prm.out = a.out;
+  prm.fin = a.final_state;
+  prm.T = a.T;
+  prm.N = a.N;
+  prm.H = a.H;
+  prm.K = a.K;
+  prm.V = a.V;
   prm.scale = a.scale;
   prm.beta_bf16 = a.beta_dtype == KDA_BF16;
   prm.init_bf16 = a.initial_dtype == KDA_BF16;
   prm.fin_bf16 = a.final_dtype == KDA_BF16;
   prm.l2norm = a.use_qk_l2norm != 0;
   prm.order = nullptr;
+  const uintptr_t al = (uintptr_t)a.q | (uintptr_t)a.k | (uintptr_t)a.v | (uintptr_t)a.g;
+  prm.pair = (a.K % 2 == 0) && (a.V % 2 == 0) && (al % 8 == 0);
+  prm.ovec = (a.V % 8 == 0) && ((uintptr_t)a.out % 16 == 0);
+  const uintptr_t sal = (uintptr_t)a.initial_state | (uintptr_t)a.final_state;
+  prm.svec = (a.K % 4 == 0) && (sal % 16 == 0);
   if (a.N >= 2 && a.N <= kPlanMaxN) {
     int32_t* order = static_cast<int32_t*>(a.workspace);
     hipLaunchKernelGGL(plan_order_kernel, dim3(1), dim3(1024), 0, stream, a.cu_seqlens, a.N, a.T, order);
@@ -648,7 +787,7 @@ hipError_t launch_chunk_prefill(const kda_prefill_args_t& a, hipStream_t stream)
     prm.order = order;
   }
   const bool bf16 = a.qkv_dtype == KDA_BF16;
-  // Fewer than ~2 workgroups per CU from (sequence, head) chains alone: split V.
+  // Few (sequence, head) chains: narrower value blocks give more workgroups.
   const int64_t chains = a.N * a.H;
   if (a.K <= 64) {
     prm.nvb = (int)((a.V + 63) / 64);

@@ -245,3 +245,21 @@ def device_cache(num_rows, H, V, K, dtype="bf16", gap=GAP, offset=0, seed=7, std
         vals = torch.randn((r1 - r0, payload), generator=gen, device=device, dtype=torch.float32) * std
         rows[r0:r1] = vals.to(view.dtype)
     return backing, offset, (num_rows, H, V, K), (stride0, V * K, K, 1)
+
+
+def e2e_copy_indices(seed, N, num_rows=4096, high_rows=31, n_high=16):
+    """Gather/scatter selection of the end-to-end prefill step.
+
+    Gather: int32, drawn with replacement (one duplicate forced), the first
+    ``n_high`` drawn from the last ``high_rows`` rows (base offset past 2^31
+    elements), 10% false flags.  Scatter: N unique int32 targets, ``n_high``
+    of them in the last rows.
+    """
+    r = rng(seed + 3)
+    gidx = r.integers(0, num_rows, size=N).astype(np.int32)
+    gidx[:n_high] = r.integers(num_rows - high_rows, num_rows, size=n_high)
+    gidx[n_high] = gidx[0]
+    flags = copy_flags(seed + 3, N, N // 10)
+    sidx = np.concatenate([np.arange(num_rows - n_high, num_rows),
+                           r.permutation(num_rows - high_rows)[:N - n_high]]).astype(np.int32)
+    return gidx, flags, sidx
