@@ -76,30 +76,28 @@ struct Cfg {
   static constexpr int KS = KP / 32;       // 32-deep contraction steps over the key dim
   static constexpr int LDK = KP + 8;       // row stride (bf16) of [64][KP] tiles
   static constexpr int LDT = kC + 8;       // row stride (bf16) of [X][64] tiles
-  static constexpr int LDA = kC + 4;       // row stride (fp32) of the [64][64] solve tile
   static constexpr int LDO = BV + 8;       // row stride (bf16) of the output staging tile
   static constexpr int SZ_ROW = kC * LDK * 2;
   static constexpr int SZ_KT = KP * LDT * 2;
   static constexpr int SZ_VT = BV * LDT * 2;
   static constexpr int SZ_T = kC * LDT * 2;
-  // LDS map (bytes).  KL, QL and KR die after the A products; their space is
-  // reused for T, -W and the output staging tile.
-  static constexpr int R_KL = 0;                    // KL [64][KP]      -> T [64][64]
+  // LDS map (bytes).  KL, QL and KR die after the A products; QL's space is
+  // reused for -W and KR's for the output staging tile.
+  static constexpr int R_KL = 0;                    // KL [64][KP]
   static constexpr int R_QL = R_KL + SZ_ROW;        // QL [64][KP]      -> -W [64][KP]
   static constexpr int R_KR = R_QL + SZ_ROW;        // KR [64][KP]      -> O staging [64][BV]
   static constexpr int R_QG = R_KR + SZ_ROW;        // Qg [64][KP]
-  static constexpr int R_KE = R_QG + SZ_ROW;        // KE^T [KP][64]
+  static constexpr int R_KE = R_QG + SZ_ROW;        // (beta K 2^gamma)^T [KP][64]
   static constexpr int R_KB = R_KE + SZ_KT;         // Kbar^T [KP][64]
   static constexpr int R_VT = R_KB + SZ_KT;         // (beta V)^T [BV][64]
-  static constexpr int R_A = R_VT + SZ_VT;          // A_kk, then T, fp32 [64][LDA]
-  static constexpr int R_AQK = R_A + kC * LDA * 4;  // A_qk bf16 [64][LDT]
+  static constexpr int R_AB = R_VT + SZ_VT;         // bf16 [64][LDT]: -A_kk below the diagonal blocks, D_b on them
+  static constexpr int R_AD = R_AB + SZ_T;          // fp32 [4][16][17]: diagonal blocks of A_kk
+  static constexpr int R_AQK = R_AD + 4 * 16 * 17 * 4;  // A_qk bf16 [64][LDT]
   static constexpr int R_TOT = R_AQK + SZ_T;        // per-wave gate sums fp32 [NW][KP]
   static constexpr int R_DEC = R_TOT + NW * KP * 4; // 2^gamma_L fp32 [KP]
   static constexpr int R_RED = R_DEC + KP * 4;      // range guard fp32 [NW]
-  static constexpr int R_X = R_RED + 64;            // solve temps fp32 [3][2][16][16]
-  static constexpr int LDS = R_X + 3 * 2 * 256 * 4;
+  static constexpr int LDS = R_RED + 64;
   static_assert(LDS <= 160 * 1024, "LDS budget");
-  static_assert(SZ_T <= SZ_ROW, "T fits in the KL region");
   static_assert(kC * LDO * 2 <= SZ_ROW, "output staging fits in the KR region");
   static_assert(RPW == 8 || RPW == 16, "rows per wave");
 };
@@ -159,6 +157,37 @@ __device__ __forceinline__ bf16x8 pack_perm(const f32x4& lo, const f32x4& hi) {
 
 __device__ __forceinline__ bf16x8 ld8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_16x16x16_bf16: A lane l holds A[l%16][4(l/16)+e], B lane l holds
+// B[4(l/16)+e][l%16] -- the same rows a C-layout lane holds, so a C tile
+// packed to bf16 is directly a B operand.
+__device__ __forceinline__ f32x4 mfma16(const s16x4& a, const s16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ s16x4 pack4(const f32x4& x) {
+  return s16x4{__builtin_bit_cast(short, (__bf16)x[0]), __builtin_bit_cast(short, (__bf16)x[1]),
+               __builtin_bit_cast(short, (__bf16)x[2]), __builtin_bit_cast(short, (__bf16)x[3])};
+}
+
+__device__ __forceinline__ s16x4 ld4s(const __bf16* p) { return *reinterpret_cast<const s16x4*>(p); }
+
+__device__ __forceinline__ f32x4 widen4(const __bf16* p) {
+  const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
+  return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+}
+
+// Workgroup barrier that orders LDS only.  __syncthreads() would also wait
+// for every outstanding global store of the wave (vmcnt(0)); the chunk loop
+// has no cross-wave traffic through global memory, so its output stores are
+// left in flight across barriers.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Ranks sequences by length, longest first (ties by index).  One workgroup.
 __global__ __launch_bounds__(1024) void plan_order_kernel(const int32_t* __restrict__ cu, int64_t N, int64_t T,
                                                           int32_t* __restrict__ order) {
@@ -208,7 +237,6 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
   static_assert(NT == BV * 4, "launch bounds");
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
   __bf16* sKL = reinterpret_cast<__bf16*>(smem + C::R_KL);
-  __bf16* sT = reinterpret_cast<__bf16*>(smem + C::R_KL);
   __bf16* sQL = reinterpret_cast<__bf16*>(smem + C::R_QL);
   __bf16* sW = reinterpret_cast<__bf16*>(smem + C::R_QL);
   __bf16* sKR = reinterpret_cast<__bf16*>(smem + C::R_KR);
@@ -217,12 +245,12 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
   __bf16* sKE = reinterpret_cast<__bf16*>(smem + C::R_KE);
   __bf16* sKB = reinterpret_cast<__bf16*>(smem + C::R_KB);
   __bf16* sVT = reinterpret_cast<__bf16*>(smem + C::R_VT);
-  float* sA = reinterpret_cast<float*>(smem + C::R_A);
+  __bf16* sAb = reinterpret_cast<__bf16*>(smem + C::R_AB);
+  float* sAd = reinterpret_cast<float*>(smem + C::R_AD);
   __bf16* sAqk = reinterpret_cast<__bf16*>(smem + C::R_AQK);
   float* sTot = reinterpret_cast<float*>(smem + C::R_TOT);
   float* sDec = reinterpret_cast<float*>(smem + C::R_DEC);
   float* sRed = reinterpret_cast<float*>(smem + C::R_RED);
-  float* sX = reinterpret_cast<float*>(smem + C::R_X);
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, provably uniform
@@ -301,7 +329,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
   int Lcap = kC;
   while (t0 < len) {
     const int L = (int)((len - t0) < (int64_t)Lcap ? (len - t0) : (int64_t)Lcap);
-    __syncthreads();  // the previous chunk's LDS readers are done
+    lds_barrier();  // the previous chunk's LDS readers are done
 
     // ---------------- phase 0: loads, (beta V)^T, gate sums, norms ----------
     // All loads are unconditional (row clamped to the last valid row, channel
@@ -430,7 +458,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
       rk[r] = p.l2norm ? __frsqrt_rn(sk + kL2Eps) : 1.f;
       rq[r] = p.l2norm ? __frsqrt_rn(sq + kL2Eps) : 1.f;
     }
-    __syncthreads();
+    lds_barrier();
 
     // gamma in log2 units, the reference row m and the range guard
     const int mw = (L > 32 ? 32 : 16) / RPW;  // waves whose rows precede the reference boundary
@@ -458,7 +486,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     }
     guard = wave_max(guard);
     if (l == 0) sRed[w] = guard;
-    __syncthreads();
+    lds_barrier();
     float gmax = sRed[0];
 #pragma unroll
     for (int ww = 1; ww < NW; ++ww) gmax = fmaxf(gmax, sRed[ww]);
@@ -468,43 +496,64 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     }
 
     // ---------------- phase A: gated operand tiles into LDS ----------------
+    {
+      float cg[CPL], cb[CPL];
 #pragma unroll
-    for (int cc = 0; cc < CPL; ++cc) {
-      const int64_t c = c_lo + cc;
-      const float cg = __builtin_amdgcn_exp2f(gm[cc]);           // 2^gamma_m
-      const float cb = __builtin_amdgcn_exp2f(gL[cc] - gm[cc]);  // 2^(gamma_L - gamma_m)
-      if (w == 0) sDec[c] = __builtin_amdgcn_exp2f(gL[cc]);
-      __bf16 ke[RPW], kb[RPW];
+      for (int cc = 0; cc < CPL; ++cc) {
+        cg[cc] = __builtin_amdgcn_exp2f(gm[cc]);           // 2^gamma_m
+        cb[cc] = __builtin_amdgcn_exp2f(gL[cc] - gm[cc]);  // 2^(gamma_L - gamma_m)
+        if (w == 0) sDec[c_lo + cc] = __builtin_amdgcn_exp2f(gL[cc]);
+      }
+      __bf16 ke[CPL][RPW], kb[CPL][RPW];
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
         const int i = RPW * w + r;
-        const float e1 = __builtin_amdgcn_exp2f(gx[r][cc] - gm[cc]);  // 2^(gamma_i - gamma_m)
-        const float e2 = __builtin_amdgcn_exp2f(gm[cc] - gx[r][cc]);  // 2^(gamma_m - gamma_i)
-        const float kh = kx[r][cc] * rk[r];
-        const float qh = qx[r][cc] * rq[r];
-        sKL[i * C::LDK + c] = (__bf16)(bt[r] * kh * e1);
-        sQL[i * C::LDK + c] = (__bf16)(scale * qh * e1);
-        sKR[i * C::LDK + c] = (__bf16)(kh * e2);
-        sQg[i * C::LDK + c] = (__bf16)(scale * qh * (e1 * cg));
-        ke[r] = (__bf16)(bt[r] * kh * (e1 * cg));
-        kb[r] = (__bf16)(kh * (e2 * cb));
+        __bf16 kl[CPL], ql[CPL], kr[CPL], qg[CPL];
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+          const float e1 = __builtin_amdgcn_exp2f(gx[r][cc] - gm[cc]);  // 2^(gamma_i - gamma_m)
+          const float e2 = __builtin_amdgcn_exp2f(gm[cc] - gx[r][cc]);  // 2^(gamma_m - gamma_i)
+          const float kh = kx[r][cc] * rk[r];
+          const float qh = qx[r][cc] * rq[r];
+          kl[cc] = (__bf16)(bt[r] * kh * e1);
+          ql[cc] = (__bf16)(scale * qh * e1);
+          kr[cc] = (__bf16)(kh * e2);
+          qg[cc] = (__bf16)(scale * qh * (e1 * cg[cc]));
+          ke[cc][r] = (__bf16)(bt[r] * kh * (e1 * cg[cc]));
+          kb[cc][r] = (__bf16)(kh * (e2 * cb[cc]));
+        }
+        if (CPL == 2) {
+          typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+          *reinterpret_cast<bf16x2*>(sKL + i * C::LDK + c_lo) = bf16x2{kl[0], kl[CPL - 1]};
+          *reinterpret_cast<bf16x2*>(sQL + i * C::LDK + c_lo) = bf16x2{ql[0], ql[CPL - 1]};
+          *reinterpret_cast<bf16x2*>(sKR + i * C::LDK + c_lo) = bf16x2{kr[0], kr[CPL - 1]};
+          *reinterpret_cast<bf16x2*>(sQg + i * C::LDK + c_lo) = bf16x2{qg[0], qg[CPL - 1]};
+        } else {
+          sKL[i * C::LDK + c_lo] = kl[0];
+          sQL[i * C::LDK + c_lo] = ql[0];
+          sKR[i * C::LDK + c_lo] = kr[0];
+          sQg[i * C::LDK + c_lo] = qg[0];
+        }
       }
       // transposed tiles: RPW consecutive rows of one channel, 16-byte stores
-      bf16x8* pe = reinterpret_cast<bf16x8*>(sKE + c * C::LDT + RPW * w);
-      bf16x8* pb = reinterpret_cast<bf16x8*>(sKB + c * C::LDT + RPW * w);
 #pragma unroll
-      for (int h8 = 0; h8 < RPW / 8; ++h8) {
-        bf16x8 xe, xb;
+      for (int cc = 0; cc < CPL; ++cc) {
+        bf16x8* pe = reinterpret_cast<bf16x8*>(sKE + (c_lo + cc) * C::LDT + RPW * w);
+        bf16x8* pb = reinterpret_cast<bf16x8*>(sKB + (c_lo + cc) * C::LDT + RPW * w);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          xe[j] = ke[8 * h8 + j];
-          xb[j] = kb[8 * h8 + j];
+        for (int h8 = 0; h8 < RPW / 8; ++h8) {
+          bf16x8 xe, xb;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            xe[j] = ke[cc][8 * h8 + j];
+            xb[j] = kb[cc][8 * h8 + j];
+          }
+          pe[h8] = xe;
+          pb[h8] = xb;
         }
-        pe[h8] = xe;
-        pb[h8] = xb;
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---------------- phase B: A_kk (fp32) and A_qk (bf16) -----------------
     // 10 lower 16x16 block pairs x {kk, qk} = 20 tile jobs, round-robin over waves.
@@ -525,110 +574,74 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
         const int row = 16 * bi + 4 * lg + e;
         if (is_qk)
           sAqk[row * C::LDT + col] = (__bf16)(row >= col ? acc[e] : 0.f);
+        else if (bi == bj)
+          sAd[(bi * 16 + 4 * lg + e) * 17 + lr] = row > col ? acc[e] : 0.f;
         else
-          sA[row * C::LDA + col] = row > col ? acc[e] : 0.f;
+          sAb[row * C::LDT + col] = (__bf16)(-acc[e]);
       }
     }
-    __syncthreads();
+    lds_barrier();
 
-    // ---------------- phase C: T = (I + A_kk)^-1, in place in sA ----------
+    // ---------------- phase C: D_b = (I + A_bb)^-1 for the diagonal blocks --
     if (w == 0) {
-      // diagonal 16x16 blocks by substitution; lane = (block, column)
+      // fp32 substitution; lane = (block, column); result stored as bf16
       const int bb = l >> 4;
       int col = l & 15;
       asm volatile("" : "+v"(col));  // keep the identity column below from being hoisted out of the chunk loop
-      float* Ab = sA + (16 * bb) * C::LDA + 16 * bb;
+      const float* Ab = sAd + bb * 16 * 17;
       float x[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) x[i] = (i == col) ? 1.f : 0.f;
 #pragma unroll
       for (int j = 0; j < 15; ++j) {
 #pragma unroll
-        for (int i = j + 1; i < 16; ++i) x[i] -= Ab[i * C::LDA + j] * x[j];
+        for (int i = j + 1; i < 16; ++i) x[i] -= Ab[i * 17 + j] * x[j];
         // bound how many triangle reads the scheduler hoists (register pressure)
         if (j % 4 == 3) __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) Ab[i * C::LDA + col] = x[i];
+      for (int i = 0; i < 16; ++i) sAb[(16 * bb + i) * C::LDT + 16 * bb + col] = (__bf16)x[i];
     }
-    __syncthreads();
-    // off-diagonal blocks, one block row at a time:
-    //   T[bi][bj] = -D_bi * sum_{k=bj}^{bi-1} A[bi][k] T[k][bj]
-    for (int bi = 1; bi < 4; ++bi) {
-      if (w < bi) {
-        const int bj = w;
-        const int r = l >> 2, c0 = 4 * (l & 3);
-        float* X = sX + w * 512;
-        float* Y = X + 256;
-        f32x4 xs = {0.f, 0.f, 0.f, 0.f};
-        for (int kb = bj; kb < bi; ++kb) {
-#pragma unroll
-          for (int kk = 0; kk < 16; ++kk) {
-            const float a = sA[(16 * bi + r) * C::LDA + 16 * kb + kk];
-            const f32x4 t4 = *reinterpret_cast<const f32x4*>(sA + (16 * kb + kk) * C::LDA + 16 * bj + c0);
-            xs += a * t4;
-          }
-        }
-        *reinterpret_cast<f32x4*>(X + r * 16 + c0) = xs;
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): X visible to the whole wave
-        __builtin_amdgcn_wave_barrier();
-        f32x4 ys = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-          const float d = sA[(16 * bi + r) * C::LDA + 16 * bi + kk];
-          const f32x4 x4 = *reinterpret_cast<const f32x4*>(X + kk * 16 + c0);
-          ys -= d * x4;
-        }
-        *reinterpret_cast<f32x4*>(Y + r * 16 + c0) = ys;
-      }
-      __syncthreads();
-      if (w < bi) {
-        const int r = l >> 2, c0 = 4 * (l & 3);
-        *reinterpret_cast<f32x4*>(sA + (16 * bi + r) * C::LDA + 16 * w + c0) =
-            *reinterpret_cast<const f32x4*>(sX + w * 512 + 256 + r * 16 + c0);
-      }
-      __syncthreads();
-    }
-    // T to bf16 [64][LDT] with zeros above the diagonal (KL is dead)
-    for (int e = tid; e < kC * kC; e += NT) {
-      const int r = e >> 6, c = e & 63;
-      sT[r * C::LDT + c] = (__bf16)(c <= r ? sA[r * C::LDA + c] : 0.f);
-    }
-    __syncthreads();
+    lds_barrier();
 
-    // ---------------- phase D: -W into LDS (QL is dead) --------------------
-    // W^T[c][i] = sum_j KE^T[c][j] T[i][j]
-    for (int ct = w; ct < C::KT; ct += NW) {
+    // ---------------- phase D: [W | U] = (I + A_kk)^-1 [beta K 2^gamma | beta V] --
+    // Blocked forward substitution, one 16-column tile at a time, no barriers:
+    //   X_b = D_b (R_b - sum_{c<b} A_bc X_c),  b = 0..3
+    // R is read from the transposed tiles (4 consecutive rows per lane = C layout).
+    auto solve_tile = [&](const __bf16* rt, f32x4 (&X)[4]) {
+      s16x4 xb[4];
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int bk = 0; bk < 4; ++bk) {
+        f32x4 acc = widen4(rt + 16 * bk + 4 * lg);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          if (32 * ks > 16 * it + 15) continue;
-          acc = mfma(ld8(sKE + (16 * ct + lr) * C::LDT + 32 * ks + 8 * lg),
-                     ld8(sT + (16 * it + lr) * C::LDT + 32 * ks + 8 * lg), acc);
-        }
-        *reinterpret_cast<bf16x4*>(sW + (16 * it + lr) * C::LDK + 16 * ct + 4 * lg) =
-            bf16x4{(__bf16)(-acc[0]), (__bf16)(-acc[1]), (__bf16)(-acc[2]), (__bf16)(-acc[3])};
+        for (int c = 0; c < bk; ++c) acc = mfma16(ld4s(sAb + (16 * bk + lr) * C::LDT + 16 * c + 4 * lg), xb[c], acc);
+        X[bk] = mfma16(ld4s(sAb + (16 * bk + lr) * C::LDT + 16 * bk + 4 * lg), pack4(acc), f32x4{0.f, 0.f, 0.f, 0.f});
+        xb[bk] = pack4(X[bk]);
       }
+    };
+    // -W into LDS (QL is dead): this wave's key-column tiles
+    for (int ct = w; ct < C::KT; ct += NW) {
+      f32x4 Xw[4];
+      solve_tile(sKE + (16 * ct + lr) * C::LDT, Xw);
+#pragma unroll
+      for (int bk = 0; bk < 4; ++bk)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sW[(16 * bk + 4 * lg + e) * C::LDK + 16 * ct + lr] = (__bf16)(-Xw[bk][e]);
     }
-    __syncthreads();
+    // U for this wave's own value columns stays in registers
+    f32x4 U[4];
+    solve_tile(sVT + (16 * w + lr) * C::LDT, U);
+    lds_barrier();
 
     // ---------------- phase E: the serial chain on this wave's 16 columns ----
-    // U = T (beta V), V_new = U - W S, O = Qg S + A_qk V_new, S = D S + Kbar^T V_new
+    // V_new = U - W S, O = Qg S + A_qk V_new, S = D S + Kbar^T V_new
     bf16x8 bS[C::KS];
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) bS[ks] = pack_perm(S[2 * ks], S[2 * ks + 1]);
     f32x4 Vn[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        if (32 * ks > 16 * rt + 15) continue;
-        acc = mfma(ld8(sT + (16 * rt + lr) * C::LDT + 32 * ks + 8 * lg),
-                   ld8(sVT + (16 * w + lr) * C::LDT + 32 * ks + 8 * lg), acc);
-      }
+      f32x4 acc = U[rt];
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) acc = mfma(ld_perm(sW + (16 * rt + lr) * C::LDK + 32 * ks + 4 * lg), bS[ks], acc);
       Vn[rt] = acc;
@@ -665,7 +678,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
       for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) sO[(16 * rt + 4 * lg + e) * C::LDO + 16 * w + lr] = (__bf16)O[rt][e];
-      __syncthreads();
+      lds_barrier();
       constexpr int VPR = BV / 8;  // 16-byte runs per row
 #pragma unroll
       for (int u0 = 0; u0 < kC * VPR; u0 += NT) {
