@@ -74,8 +74,12 @@ struct Cfg {
   static constexpr int VPL = BV / 64;      // value columns per lane, elementwise phase
   static constexpr int KT = KP / 16;       // 16-row key tiles
   static constexpr int KS = KP / 32;       // 32-deep contraction steps over the key dim
-  static constexpr int LDK = KP + 8;       // row stride (bf16) of [64][KP] tiles
-  static constexpr int LDT = kC + 8;       // row stride (bf16) of [X][64] tiles
+  // Row strides (bf16 elements), chosen so the lanes of one LDS pass hit
+  // distinct banks: tiles read 16 bytes per lane use a stride of 4 (mod 32)
+  // dwords, tiles read 8 bytes per lane a stride of 2 (mod 32) dwords.
+  static constexpr int LDK = KP + 8;       // [64][KP] tiles read 16 B/lane (KL, QL, KR)
+  static constexpr int LDKE = KP + 4;      // [64][KP] tiles read 8 B/lane (Qg, -W)
+  static constexpr int LDT = kC + 4;       // [X][64] tiles, read 8 B/lane
   static constexpr int LDO = BV + 8;       // row stride (bf16) of the output staging tile
   static constexpr int SZ_ROW = kC * LDK * 2;
   static constexpr int SZ_KT = KP * LDT * 2;
@@ -230,6 +234,16 @@ struct Params {
   int svec;              // K % 4 == 0 and state pointers aligned: vector state I/O
 };
 
+// Raw bits of one chunk's inputs as loaded (bf16 pairs packed in one word),
+// kept in registers from the time the loads are issued until phase 0.
+template <int RPW, int CPL, int VPL, bool kBF16>
+struct RawChunk {
+  static constexpr int KW = (kBF16 && CPL == 2) ? 1 : CPL;  // words per row of q/k
+  static constexpr int VW = (kBF16 && VPL == 2) ? 1 : VPL;  // words per row of v
+  unsigned k[RPW][KW], q[RPW][KW], v[RPW][VW], b[RPW];
+  float g[RPW][CPL];
+};
+
 template <int KP, int BV, bool kBF16>
 __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
   using C = Cfg<KP, BV>;
@@ -325,111 +339,182 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
   const float scale = p.scale;
   const int64_t c_lo = (int64_t)l * CPL;       // first key channel of this lane (elementwise phase)
   const int64_t vc_lo = v0 + (int64_t)l * VPL; // first value column of this lane (elementwise phase)
-  int64_t t0 = 0;
-  int Lcap = kC;
-  while (t0 < len) {
-    const int L = (int)((len - t0) < (int64_t)Lcap ? (len - t0) : (int64_t)Lcap);
-    lds_barrier();  // the previous chunk's LDS readers are done
-
-    // ---------------- phase 0: loads, (beta V)^T, gate sums, norms ----------
-    // All loads are unconditional (row clamped to the last valid row, channel
-    // to the last valid channel) so they are in flight together; values
-    // outside the chunk or the key/value range are zeroed afterwards.
-    float kx[RPW][CPL], qx[RPW][CPL], gx[RPW][CPL], vx[RPW][VPL], bt[RPW];
+  // Loads of one chunk's rows [tb, tb + min(64, len - tb)): every load is
+  // unconditional (row clamped to the span's last row, channel to the last
+  // valid one) so they are all in flight together; values outside the chunk
+  // or the key/value range are zeroed in phase 0.
+  using Raw = RawChunk<RPW, CPL, VPL, kBF16>;
+  Raw raw;
+  auto issue_loads = [&](int64_t tb) {
+    const int64_t span = (len - tb) < (int64_t)kC ? (len - tb) : (int64_t)kC;
     int64_t th[RPW];
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       const int i = RPW * w + r;
-      th[r] = (bos + t0 + (i < L ? i : L - 1)) * H + h;
+      th[r] = (bos + tb + (i < span ? i : span - 1)) * H + h;
     }
     if (p.beta_bf16) {
 #pragma unroll
-      for (int r = 0; r < RPW; ++r) bt[r] = bf2f(static_cast<const unsigned short*>(p.beta)[th[r]]);
+      for (int r = 0; r < RPW; ++r) raw.b[r] = (unsigned)static_cast<const unsigned short*>(p.beta)[th[r]] << 16;
     } else {
 #pragma unroll
-      for (int r = 0; r < RPW; ++r) bt[r] = static_cast<const float*>(p.beta)[th[r]];
+      for (int r = 0; r < RPW; ++r) raw.b[r] = static_cast<const unsigned*>(p.beta)[th[r]];
     }
-    if (CPL == 2 && p.pair) {
-      const int64_t cs = c_lo + 1 < K ? c_lo : K - 2;
+    if (p.pair) {
+      // two key channels (CPL == 2) / value columns (VPL == 2) per access
+      const int64_t cs = CPL == 2 ? (c_lo + 1 < K ? c_lo : K - 2) : (c_lo < K ? c_lo : K - 1);
+      const int64_t vs = VPL == 2 ? (vc_lo + 1 < V ? vc_lo : V - 2) : (vc_lo < V ? vc_lo : V - 1);
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
         if (kBF16) {
-          const unsigned wk = *reinterpret_cast<const unsigned*>(static_cast<const unsigned short*>(p.k) + th[r] * K + cs);
-          const unsigned wq = *reinterpret_cast<const unsigned*>(static_cast<const unsigned short*>(p.q) + th[r] * K + cs);
-          kx[r][0] = __uint_as_float(wk << 16);
-          kx[r][CPL - 1] = __uint_as_float(wk & 0xffff0000u);
-          qx[r][0] = __uint_as_float(wq << 16);
-          qx[r][CPL - 1] = __uint_as_float(wq & 0xffff0000u);
+          const unsigned short* k16 = static_cast<const unsigned short*>(p.k) + th[r] * K + cs;
+          const unsigned short* q16 = static_cast<const unsigned short*>(p.q) + th[r] * K + cs;
+          const unsigned short* v16 = static_cast<const unsigned short*>(p.v) + th[r] * V + vs;
+          if (CPL == 2) {
+            raw.k[r][0] = *reinterpret_cast<const unsigned*>(k16);
+            raw.q[r][0] = *reinterpret_cast<const unsigned*>(q16);
+          } else {
+            raw.k[r][0] = *k16;
+            raw.q[r][0] = *q16;
+          }
+          if (VPL == 2)
+            raw.v[r][0] = *reinterpret_cast<const unsigned*>(v16);
+          else
+            raw.v[r][0] = *v16;
         } else {
-          const float2 fk = *reinterpret_cast<const float2*>(static_cast<const float*>(p.k) + th[r] * K + cs);
-          const float2 fq = *reinterpret_cast<const float2*>(static_cast<const float*>(p.q) + th[r] * K + cs);
-          kx[r][0] = fk.x;
-          kx[r][CPL - 1] = fk.y;
-          qx[r][0] = fq.x;
-          qx[r][CPL - 1] = fq.y;
+          const unsigned* k32 = static_cast<const unsigned*>(p.k) + th[r] * K + cs;
+          const unsigned* q32 = static_cast<const unsigned*>(p.q) + th[r] * K + cs;
+          const unsigned* v32 = static_cast<const unsigned*>(p.v) + th[r] * V + vs;
+          if (CPL == 2) {
+            const uint2 a = *reinterpret_cast<const uint2*>(k32), c = *reinterpret_cast<const uint2*>(q32);
+            raw.k[r][0] = a.x; raw.k[r][CPL - 1] = a.y;
+            raw.q[r][0] = c.x; raw.q[r][CPL - 1] = c.y;
+          } else {
+            raw.k[r][0] = *k32;
+            raw.q[r][0] = *q32;
+          }
+          if (VPL == 2) {
+            const uint2 a = *reinterpret_cast<const uint2*>(v32);
+            raw.v[r][0] = a.x; raw.v[r][VPL - 1] = a.y;
+          } else {
+            raw.v[r][0] = *v32;
+          }
         }
-        const float2 fg = *reinterpret_cast<const float2*>(p.g + th[r] * K + cs);
-        gx[r][0] = fg.x;
-        gx[r][CPL - 1] = fg.y;
+        if (CPL == 2) {
+          const float2 fg = *reinterpret_cast<const float2*>(p.g + th[r] * K + cs);
+          raw.g[r][0] = fg.x;
+          raw.g[r][CPL - 1] = fg.y;
+        } else {
+          raw.g[r][0] = p.g[th[r] * K + cs];
+        }
       }
     } else {
+      // element by element (odd K or V, or unaligned tensors); bf16 pairs are
+      // packed after the loads return
 #pragma unroll
-      for (int r = 0; r < RPW; ++r)
+      for (int r = 0; r < RPW; ++r) {
+        unsigned kk[CPL], qq[CPL], vv2[VPL];
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) {
           const int64_t cs = c_lo + cc < K ? c_lo + cc : K - 1;
-          kx[r][cc] = ld_in<kBF16>(p.k, th[r] * K + cs);
-          qx[r][cc] = ld_in<kBF16>(p.q, th[r] * K + cs);
-          gx[r][cc] = p.g[th[r] * K + cs];
+          kk[cc] = kBF16 ? (unsigned)static_cast<const unsigned short*>(p.k)[th[r] * K + cs]
+                         : static_cast<const unsigned*>(p.k)[th[r] * K + cs];
+          qq[cc] = kBF16 ? (unsigned)static_cast<const unsigned short*>(p.q)[th[r] * K + cs]
+                         : static_cast<const unsigned*>(p.q)[th[r] * K + cs];
+          raw.g[r][cc] = p.g[th[r] * K + cs];
         }
-    }
-    if (VPL == 2 && p.pair) {
-      const int64_t vs = vc_lo + 1 < V ? vc_lo : V - 2;
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        if (kBF16) {
-          const unsigned wv = *reinterpret_cast<const unsigned*>(static_cast<const unsigned short*>(p.v) + th[r] * V + vs);
-          vx[r][0] = __uint_as_float(wv << 16);
-          vx[r][VPL - 1] = __uint_as_float(wv & 0xffff0000u);
-        } else {
-          const float2 fv = *reinterpret_cast<const float2*>(static_cast<const float*>(p.v) + th[r] * V + vs);
-          vx[r][0] = fv.x;
-          vx[r][VPL - 1] = fv.y;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < RPW; ++r)
 #pragma unroll
         for (int vv = 0; vv < VPL; ++vv) {
           const int64_t vs = vc_lo + vv < V ? vc_lo + vv : V - 1;
-          vx[r][vv] = ld_in<kBF16>(p.v, th[r] * V + vs);
+          vv2[vv] = kBF16 ? (unsigned)static_cast<const unsigned short*>(p.v)[th[r] * V + vs]
+                          : static_cast<const unsigned*>(p.v)[th[r] * V + vs];
         }
+        if (kBF16 && CPL == 2) {
+          raw.k[r][0] = kk[0] | (kk[CPL - 1] << 16);
+          raw.q[r][0] = qq[0] | (qq[CPL - 1] << 16);
+        } else {
+#pragma unroll
+          for (int cc = 0; cc < Raw::KW; ++cc) {
+            raw.k[r][cc] = kk[cc];
+            raw.q[r][cc] = qq[cc];
+          }
+        }
+        if (kBF16 && VPL == 2) {
+          raw.v[r][0] = vv2[0] | (vv2[VPL - 1] << 16);
+        } else {
+#pragma unroll
+          for (int vv = 0; vv < Raw::VW; ++vv) raw.v[r][vv] = vv2[vv];
+        }
+      }
     }
+  };
+
+  int64_t t0 = 0;
+  int Lcap = kC;
+  if (len > 0) issue_loads(0);
+  while (t0 < len) {
+    const int L = (int)((len - t0) < (int64_t)Lcap ? (len - t0) : (int64_t)Lcap);
+    lds_barrier();  // the previous chunk's LDS readers are done
+    // Per-iteration copies of the lane indices, opaque to the optimiser: this
+    // keeps every lane-dependent LDS address from being hoisted out of the
+    // loop into a register of its own (which would force spills).
+    int tid_i = tid;
+    asm volatile("" : "+v"(tid_i));
+    const int l = tid_i & 63;
+    const int lr = l & 15;
+    const int lg = l >> 4;
+    const int64_t c_lo = (int64_t)l * CPL;
+    const int64_t vc_lo = v0 + (int64_t)l * VPL;
+    const int tid_l = tid_i;
+
+    // ---------------- phase 0: loads, (beta V)^T, gate sums, norms ----------
+    // The chunk's rows were loaded by issue_loads (for this chunk's start) while
+    // the previous chunk computed; unpack them and zero what lies outside.
+    float kx[RPW][CPL], qx[RPW][CPL], gx[RPW][CPL], vx[RPW][VPL], bt[RPW];
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       const bool okr = RPW * w + r < L;
-      bt[r] = okr ? bt[r] : 0.f;
+      bt[r] = okr ? __uint_as_float(raw.b[r]) : 0.f;
 #pragma unroll
       for (int cc = 0; cc < CPL; ++cc) {
+        float kv, qv;
+        if (kBF16 && CPL == 2) {
+          kv = __uint_as_float(cc == 0 ? raw.k[r][0] << 16 : raw.k[r][0] & 0xffff0000u);
+          qv = __uint_as_float(cc == 0 ? raw.q[r][0] << 16 : raw.q[r][0] & 0xffff0000u);
+        } else if (kBF16) {
+          kv = __uint_as_float(raw.k[r][cc] << 16);
+          qv = __uint_as_float(raw.q[r][cc] << 16);
+        } else {
+          kv = __uint_as_float(raw.k[r][cc]);
+          qv = __uint_as_float(raw.q[r][cc]);
+        }
         const bool okc = okr && c_lo + cc < K;
-        kx[r][cc] = okc ? kx[r][cc] : 0.f;
-        qx[r][cc] = okc ? qx[r][cc] : 0.f;
-        gx[r][cc] = okc ? gx[r][cc] : 0.f;
+        kx[r][cc] = okc ? kv : 0.f;
+        qx[r][cc] = okc ? qv : 0.f;
+        gx[r][cc] = okc ? raw.g[r][cc] : 0.f;
       }
 #pragma unroll
-      for (int vv = 0; vv < VPL; ++vv) vx[r][vv] = (okr && vc_lo + vv < V) ? vx[r][vv] : 0.f;
+      for (int vv = 0; vv < VPL; ++vv) {
+        float x;
+        if (kBF16 && VPL == 2)
+          x = __uint_as_float(vv == 0 ? raw.v[r][0] << 16 : raw.v[r][0] & 0xffff0000u);
+        else if (kBF16)
+          x = __uint_as_float(raw.v[r][vv] << 16);
+        else
+          x = __uint_as_float(raw.v[r][vv]);
+        vx[r][vv] = (okr && vc_lo + vv < V) ? x : 0.f;
+      }
     }
     // (beta V)^T: this lane's RPW consecutive rows of each of its value columns
 #pragma unroll
     for (int vv = 0; vv < VPL; ++vv) {
-      bf16x8* pv = reinterpret_cast<bf16x8*>(sVT + (l * VPL + vv) * C::LDT + RPW * w);
+      bf16x4* pv = reinterpret_cast<bf16x4*>(sVT + (l * VPL + vv) * C::LDT + RPW * w);
 #pragma unroll
-      for (int h8 = 0; h8 < RPW / 8; ++h8) {
-        bf16x8 x;
+      for (int h4 = 0; h4 < RPW / 4; ++h4) {
+        bf16x4 x;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = (__bf16)(bt[8 * h8 + j] * vx[8 * h8 + j][vv]);
-        pv[h8] = x;
+        for (int j = 0; j < 4; ++j) x[j] = (__bf16)(bt[4 * h4 + j] * vx[4 * h4 + j][vv]);
+        pv[h4] = x;
       }
     }
     // inclusive sum of g over this wave's rows
@@ -527,60 +612,82 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
           *reinterpret_cast<bf16x2*>(sKL + i * C::LDK + c_lo) = bf16x2{kl[0], kl[CPL - 1]};
           *reinterpret_cast<bf16x2*>(sQL + i * C::LDK + c_lo) = bf16x2{ql[0], ql[CPL - 1]};
           *reinterpret_cast<bf16x2*>(sKR + i * C::LDK + c_lo) = bf16x2{kr[0], kr[CPL - 1]};
-          *reinterpret_cast<bf16x2*>(sQg + i * C::LDK + c_lo) = bf16x2{qg[0], qg[CPL - 1]};
+          *reinterpret_cast<bf16x2*>(sQg + i * C::LDKE + c_lo) = bf16x2{qg[0], qg[CPL - 1]};
         } else {
           sKL[i * C::LDK + c_lo] = kl[0];
           sQL[i * C::LDK + c_lo] = ql[0];
           sKR[i * C::LDK + c_lo] = kr[0];
-          sQg[i * C::LDK + c_lo] = qg[0];
+          sQg[i * C::LDKE + c_lo] = qg[0];
         }
       }
       // transposed tiles: RPW consecutive rows of one channel, 16-byte stores
 #pragma unroll
       for (int cc = 0; cc < CPL; ++cc) {
-        bf16x8* pe = reinterpret_cast<bf16x8*>(sKE + (c_lo + cc) * C::LDT + RPW * w);
-        bf16x8* pb = reinterpret_cast<bf16x8*>(sKB + (c_lo + cc) * C::LDT + RPW * w);
+        bf16x4* pe = reinterpret_cast<bf16x4*>(sKE + (c_lo + cc) * C::LDT + RPW * w);
+        bf16x4* pb = reinterpret_cast<bf16x4*>(sKB + (c_lo + cc) * C::LDT + RPW * w);
 #pragma unroll
-        for (int h8 = 0; h8 < RPW / 8; ++h8) {
-          bf16x8 xe, xb;
+        for (int h4 = 0; h4 < RPW / 4; ++h4) {
+          bf16x4 xe, xb;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            xe[j] = ke[cc][8 * h8 + j];
-            xb[j] = kb[cc][8 * h8 + j];
+          for (int j = 0; j < 4; ++j) {
+            xe[j] = ke[cc][4 * h4 + j];
+            xb[j] = kb[cc][4 * h4 + j];
           }
-          pe[h8] = xe;
-          pb[h8] = xb;
+          pe[h4] = xe;
+          pb[h4] = xb;
         }
       }
     }
     lds_barrier();
 
     // ---------------- phase B: A_kk (fp32) and A_qk (bf16) -----------------
-    // 10 lower 16x16 block pairs x {kk, qk} = 20 tile jobs, round-robin over waves.
-    for (int job = w; job < 20; job += NW) {
-      const int pair = job >> 1;
-      const bool is_qk = job & 1;
-      const int bi = pair >= 6 ? 3 : (pair >= 3 ? 2 : (pair >= 1 ? 1 : 0));
-      const int bj = pair - (bi * (bi + 1)) / 2;
-      const __bf16* left = is_qk ? sQL : sKL;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // 10 lower 16x16 block pairs (bi >= bj), round-robin over waves; A_kk and
+    // A_qk of a pair share the right operand, and a wave's pairs run as
+    // interleaved independent accumulator chains.
+    {
+      constexpr int MP = (10 + NW - 1) / NW;  // pairs per wave at most
+      f32x4 akk[MP], aqk[MP];
+#pragma unroll
+      for (int m = 0; m < MP; ++m) {
+        akk[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        aqk[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks)
-        acc = mfma(ld8(left + (16 * bi + lr) * C::LDK + 32 * ks + 8 * lg),
-                   ld8(sKR + (16 * bj + lr) * C::LDK + 32 * ks + 8 * lg), acc);
-      const int col = 16 * bj + lr;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 16 * bi + 4 * lg + e;
-        if (is_qk)
-          sAqk[row * C::LDT + col] = (__bf16)(row >= col ? acc[e] : 0.f);
-        else if (bi == bj)
-          sAd[(bi * 16 + 4 * lg + e) * 17 + lr] = row > col ? acc[e] : 0.f;
-        else
-          sAb[row * C::LDT + col] = (__bf16)(-acc[e]);
+        for (int m = 0; m < MP; ++m) {
+          const int pr = w + m * NW;
+          if (pr < 10) {
+            const int bi = pr >= 6 ? 3 : (pr >= 3 ? 2 : (pr >= 1 ? 1 : 0));
+            const int bj = pr - (bi * (bi + 1)) / 2;
+            const bf16x8 rgt = ld8(sKR + (16 * bj + lr) * C::LDK + 32 * ks + 8 * lg);
+            akk[m] = mfma(ld8(sKL + (16 * bi + lr) * C::LDK + 32 * ks + 8 * lg), rgt, akk[m]);
+            aqk[m] = mfma(ld8(sQL + (16 * bi + lr) * C::LDK + 32 * ks + 8 * lg), rgt, aqk[m]);
+          }
+        }
+#pragma unroll
+      for (int m = 0; m < MP; ++m) {
+        const int pr = w + m * NW;
+        if (pr < 10) {
+          const int bi = pr >= 6 ? 3 : (pr >= 3 ? 2 : (pr >= 1 ? 1 : 0));
+          const int bj = pr - (bi * (bi + 1)) / 2;
+          const int col = 16 * bj + lr;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int row = 16 * bi + 4 * lg + e;
+            sAqk[row * C::LDT + col] = (__bf16)(row >= col ? aqk[m][e] : 0.f);
+            if (bi == bj)
+              sAd[(bi * 16 + 4 * lg + e) * 17 + lr] = row > col ? akk[m][e] : 0.f;
+            else
+              sAb[row * C::LDT + col] = (__bf16)(-akk[m][e]);
+          }
+        }
       }
     }
     lds_barrier();
+
+    // the next chunk's loads are issued now and land while phases C-E compute
+    if (t0 + L < len) issue_loads(t0 + L);
 
     // ---------------- phase C: D_b = (I + A_bb)^-1 for the diagonal blocks --
     if (w == 0) {
@@ -608,29 +715,54 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     // Blocked forward substitution, one 16-column tile at a time, no barriers:
     //   X_b = D_b (R_b - sum_{c<b} A_bc X_c),  b = 0..3
     // R is read from the transposed tiles (4 consecutive rows per lane = C layout).
-    auto solve_tile = [&](const __bf16* rt, f32x4 (&X)[4]) {
-      s16x4 xb[4];
+    // The wave's key-column tiles (-> W) and its own value tile (-> U) are
+    // solved together, as independent interleaved chains.
+    constexpr int NWT = (C::KT + NW - 1) / NW;  // W tiles per wave at most
+    f32x4 X[NWT + 1][4];
+    {
+      const __bf16* rhs[NWT + 1];
+      bool on[NWT + 1];
+#pragma unroll
+      for (int m = 0; m < NWT; ++m) {
+        const int ct = w + m * NW;
+        on[m] = ct < C::KT;
+        rhs[m] = sKE + (16 * (on[m] ? ct : 0) + lr) * C::LDT;
+      }
+      on[NWT] = true;
+      rhs[NWT] = sVT + (16 * w + lr) * C::LDT;
+      s16x4 xb[NWT + 1][4];
 #pragma unroll
       for (int bk = 0; bk < 4; ++bk) {
-        f32x4 acc = widen4(rt + 16 * bk + 4 * lg);
+        f32x4 acc[NWT + 1];
 #pragma unroll
-        for (int c = 0; c < bk; ++c) acc = mfma16(ld4s(sAb + (16 * bk + lr) * C::LDT + 16 * c + 4 * lg), xb[c], acc);
-        X[bk] = mfma16(ld4s(sAb + (16 * bk + lr) * C::LDT + 16 * bk + 4 * lg), pack4(acc), f32x4{0.f, 0.f, 0.f, 0.f});
-        xb[bk] = pack4(X[bk]);
+        for (int m = 0; m <= NWT; ++m) acc[m] = widen4(rhs[m] + 16 * bk + 4 * lg);
+#pragma unroll
+        for (int c = 0; c < bk; ++c) {
+          const s16x4 a = ld4s(sAb + (16 * bk + lr) * C::LDT + 16 * c + 4 * lg);
+#pragma unroll
+          for (int m = 0; m <= NWT; ++m) acc[m] = mfma16(a, xb[m][c], acc[m]);
+        }
+        const s16x4 d = ld4s(sAb + (16 * bk + lr) * C::LDT + 16 * bk + 4 * lg);
+#pragma unroll
+        for (int m = 0; m <= NWT; ++m) {
+          X[m][bk] = mfma16(d, pack4(acc[m]), f32x4{0.f, 0.f, 0.f, 0.f});
+          xb[m][bk] = pack4(X[m][bk]);
+        }
       }
-    };
-    // -W into LDS (QL is dead): this wave's key-column tiles
-    for (int ct = w; ct < C::KT; ct += NW) {
-      f32x4 Xw[4];
-      solve_tile(sKE + (16 * ct + lr) * C::LDT, Xw);
+      // -W into LDS (QL is dead)
 #pragma unroll
-      for (int bk = 0; bk < 4; ++bk)
+      for (int m = 0; m < NWT; ++m) {
+        const int ct = w + m * NW;
+        if (on[m]) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sW[(16 * bk + 4 * lg + e) * C::LDK + 16 * ct + lr] = (__bf16)(-Xw[bk][e]);
+          for (int bk = 0; bk < 4; ++bk)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sW[(16 * bk + 4 * lg + e) * C::LDKE + 16 * ct + lr] = (__bf16)(-X[m][bk][e]);
+        }
+      }
     }
     // U for this wave's own value columns stays in registers
-    f32x4 U[4];
-    solve_tile(sVT + (16 * w + lr) * C::LDT, U);
+    f32x4 (&U)[4] = X[NWT];
     lds_barrier();
 
     // ---------------- phase E: the serial chain on this wave's 16 columns ----
@@ -638,38 +770,49 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     bf16x8 bS[C::KS];
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) bS[ks] = pack_perm(S[2 * ks], S[2 * ks + 1]);
+    // Contraction step outer, row tile inner: the four accumulators of each
+    // product advance together, so consecutive MFMAs are independent.
     f32x4 Vn[4];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      f32x4 acc = U[rt];
+    for (int rt = 0; rt < 4; ++rt) Vn[rt] = U[rt];
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) acc = mfma(ld_perm(sW + (16 * rt + lr) * C::LDK + 32 * ks + 4 * lg), bS[ks], acc);
-      Vn[rt] = acc;
+    for (int ks = 0; ks < C::KS; ++ks) {
+      bf16x8 a[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) a[rt] = ld_perm(sW + (16 * rt + lr) * C::LDKE + 32 * ks + 4 * lg);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) Vn[rt] = mfma(a[rt], bS[ks], Vn[rt]);
     }
     bf16x8 bV[2];
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) bV[q2] = pack_perm(Vn[2 * q2], Vn[2 * q2 + 1]);
+    __builtin_amdgcn_sched_barrier(0);
     f32x4 O[4];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int rt = 0; rt < 4; ++rt) O[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) acc = mfma(ld_perm(sQg + (16 * rt + lr) * C::LDK + 32 * ks + 4 * lg), bS[ks], acc);
+    for (int ks = 0; ks < C::KS; ++ks) {
+      bf16x8 a[4];
 #pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
+      for (int rt = 0; rt < 4; ++rt) a[rt] = ld_perm(sQg + (16 * rt + lr) * C::LDKE + 32 * ks + 4 * lg);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) O[rt] = mfma(a[rt], bS[ks], O[rt]);
+    }
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
         if (32 * q2 > 16 * rt + 15) continue;
-        acc = mfma(ld_perm(sAqk + (16 * rt + lr) * C::LDT + 32 * q2 + 4 * lg), bV[q2], acc);
+        O[rt] = mfma(ld_perm(sAqk + (16 * rt + lr) * C::LDT + 32 * q2 + 4 * lg), bV[q2], O[rt]);
       }
-      O[rt] = acc;
-    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ct = 0; ct < C::KT; ++ct) {
-      const f32x4 dec = *reinterpret_cast<const f32x4*>(sDec + 16 * ct + 4 * lg);
-      f32x4 acc = S[ct] * dec;
+    for (int ct = 0; ct < C::KT; ++ct) S[ct] *= *reinterpret_cast<const f32x4*>(sDec + 16 * ct + 4 * lg);
 #pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) acc = mfma(ld_perm(sKB + (16 * ct + lr) * C::LDT + 32 * q2 + 4 * lg), bV[q2], acc);
-      S[ct] = acc;
-    }
+    for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+      for (int ct = 0; ct < C::KT; ++ct)
+        S[ct] = mfma(ld_perm(sKB + (16 * ct + lr) * C::LDT + 32 * q2 + 4 * lg), bV[q2], S[ct]);
 
     // ---------------- output rows of this chunk ---------------------------
     if (kBF16 && p.ovec) {
@@ -682,7 +825,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
       constexpr int VPR = BV / 8;  // 16-byte runs per row
 #pragma unroll
       for (int u0 = 0; u0 < kC * VPR; u0 += NT) {
-        const int u = u0 + tid;
+        const int u = u0 + tid_l;
         const int i = u / VPR, cv = u - i * VPR;
         if (i < L && v0 + 8 * cv < V) {
           const int64_t o = ((bos + t0 + i) * H + h) * V + v0 + 8 * cv;
