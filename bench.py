@@ -131,6 +131,105 @@ def calibrate_copy(device, gib: float = 1.0):
     print(json.dumps({"calibration_copy_bytes_read": n * 2, "calibration_copy_bytes_written": n * 2}))
 
 
+def _timed(fn, steps, warmup):
+    """Run fn() warmup + steps times; HIP events on the current stream around each call."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall * 1e3 / steps, float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def bench_other(args, dev):
+    """Secondary workloads (not the headline line): varlen, long, copy."""
+    import torch
+    import kda_recurrent_state_amd as kda
+    import kda_workloads as wl
+    base = {"metric": METRIC, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+    if args.workload == "copy":
+        nrows = 1024
+        back, off, shape, strides = wl.device_cache(nrows, H, V, K, dtype="f32", gap=wl.GAP, offset=1024,
+                                                    seed=args.seed, device=dev)
+        cache = torch.as_strided(back.view(torch.float32), shape, strides, off)
+        S = 256
+        res = {}
+        for it in ("int32", "int64"):
+            gidx = wl.copy_indices(args.seed, S, nrows, 13, it, unique=False, huge=True)
+            flags = wl.copy_flags(args.seed, S, 26)
+            sidx = wl.copy_indices(args.seed + 1, S, nrows, 13, it, unique=True, huge=True)
+            gi, fl, si = (torch.from_numpy(x).to(dev) for x in (gidx, flags, sidx))
+            packed = torch.empty((S, H, V, K), dtype=torch.float32, device=dev)
+            payload = H * V * K * 4
+            n_read = int(((gidx >= 0) & (gidx < nrows) & (flags != 0)).sum())
+            n_valid = int(((sidx >= 0) & (sidx < nrows)).sum())
+            _, g_ms = _timed(lambda: kda.kda_state_gather(cache, gi, fl, packed), args.steps, args.warmup)
+            _, s_ms = _timed(lambda: kda.kda_state_scatter(cache, si, packed), args.steps, args.warmup)
+            res[it] = {"gather_GBps": (n_read + S) * payload / (g_ms * 1e-3) / 1e9,
+                       "scatter_GBps": 2 * n_valid * payload / (s_ms * 1e-3) / 1e9, "gather_ms": g_ms, "scatter_ms": s_ms}
+        gb = float(np.mean([r["gather_GBps"] for r in res.values()]))
+        sb = float(np.mean([r["scatter_GBps"] for r in res.values()]))
+        base.update({"metric": "state gather/scatter GB/s, 1 GPU", "unit": "GB/s", "value": (gb + sb) / 2,
+                     "dtype": "f32", "ms_per_step": None,
+                     "config": {"workload": "state copy: fp32 cache [1024,32,128,128], row stride payload+4096, "
+                                            "S=256, 13 invalid indices, 26 false flags", "seq_len": None},
+                     "roofline": {"bound": "hbm", "achieved": (gb + sb) / 2, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                  "frac": (gb + sb) / 2 / HBM_PEAK_GBPS, "traffic": None,
+                                  "kernel": "state_copy_kernel"},
+                     "per_index_type": res})
+        return base
+    if args.workload == "varlen":
+        lengths = wl.lengths_varlen(args.seed)
+        inp = wl.device_prefill_inputs(lengths, H, K, V, dtype="bf16", seed=args.seed, device=dev, init_dtype="f32")
+        T, N = inp["T"], inp["N"]
+        out = torch.empty_like(inp["v"])
+        fin = torch.empty((N, H, V, K), dtype=torch.float32, device=dev)
+        ws = torch.empty(4096, dtype=torch.uint8, device=dev)
+        fn = lambda: kda.kda_chunk_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],  # noqa: E731
+                                           inp["cu_seqlens"], initial_state=inp["initial"], out=out,
+                                           final_state=fin, workspace=ws)
+        nbytes = T * H * (2 * K + 2 * K + 2 * V + 4 * K + 4 + 2 * V) + N * H * 2 * K * V * 4
+        desc = "varlen chunk prefill: 16 sequences, lengths U[512,4096], H=32, K=V=128, fp32 states"
+    else:
+        lengths = wl.lengths_long()
+        inp = wl.device_prefill_inputs(lengths, H, K, V, dtype="bf16", seed=args.seed, device=dev, initial=False)
+        T, N = inp["T"], inp["N"]
+        back, off, shape, strides = wl.device_cache(4, H, V, K, dtype="bf16", gap=wl.GAP, offset=0,
+                                                    seed=args.seed + 1, device=dev)
+        cache = torch.as_strided(back.view(torch.bfloat16), shape, strides, off)
+        gi = torch.tensor([1], dtype=torch.int32, device=dev)
+        si = torch.tensor([3], dtype=torch.int32, device=dev)
+        fl = torch.ones(1, dtype=torch.uint8, device=dev)
+        pin = torch.empty((1, H, V, K), dtype=torch.bfloat16, device=dev)
+        pout = torch.empty_like(pin)
+        out = torch.empty_like(inp["v"])
+
+        def fn():
+            kda.kda_state_gather(cache, gi, fl, pin)
+            kda.kda_chunk_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["cu_seqlens"],
+                                  initial_state=pin, out=out, final_state=pout)
+            kda.kda_state_scatter(cache, si, pout)
+        nbytes = T * H * (2 * K + 2 * K + 2 * V + 4 * K + 4 + 2 * V) + N * H * 2 * K * V * 2
+        desc = "long prefill: one 65536-token sequence, H=32, K=V=128, state gathered from / scattered to bf16 cache rows"
+    ms_wall, ms_ev = _timed(fn, args.steps, args.warmup)
+    base.update({"value": T / (ms_wall * 1e-3), "ms_per_step": ms_wall,
+                 "config": {"workload": desc, "tokens": T, "global_batch": N, "seq_len": T, "seed": args.seed},
+                 "roofline": {"bound": "hbm", "achieved": nbytes / (ms_ev * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
+                              "unit": "GB/s", "frac": nbytes / (ms_ev * 1e-3) / 1e9 / HBM_PEAK_GBPS, "traffic": None,
+                              "kernel": "kda_chunk_prefill" + (" (+ copies)" if args.workload == "long" else ""),
+                              "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": ms_ev}})
+    return base
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +239,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true", help="run only a plain 1 GiB device copy")
+    ap.add_argument("--workload", default="e2e", choices=["e2e", "varlen", "long", "copy"],
+                    help="e2e (default, the headline step); varlen / long: the chunk prefill on 16 sequences of "
+                         "512-4096 tokens / one 65536-token sequence (state gathered from and scattered to a bf16 "
+                         "cache for long); copy: state gather/scatter on an fp32 [1024,32,128,128] cache")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -158,6 +261,10 @@ def main():
     dev = torch.device("cuda:0")
     if args.calibrate_copy:
         calibrate_copy(dev)
+        return
+
+    if args.workload != "e2e":
+        print(json.dumps(bench_other(args, dev)))
         return
 
     w = build_workload(args.seed, dev)

@@ -232,6 +232,8 @@ struct Params {
   int pair;              // K, V even and q/k/v/g 8-byte aligned: two channels per load
   int ovec;              // V % 8 == 0 and out 16-byte aligned: 16-byte output stores
   int svec;              // K % 4 == 0 and state pointers aligned: vector state I/O
+  int v_zero;            // values are all zero (v is not read)
+  int init_identity;     // initial state is the identity (K == V); init is not read
 };
 
 // Raw bits of one chunk's inputs as loaded (bf16 pairs packed in one word),
@@ -301,7 +303,12 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
 
   // ---- initial state, MFMA C layout: S[ct][e] = S(c = 16ct + 4lg + e, vcol) ----
   f32x4 S[C::KT];
-  if (p.init) {
+  if (p.init_identity) {
+#pragma unroll
+    for (int ct = 0; ct < C::KT; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[ct][e] = (16 * ct + 4 * lg + e == vcol && vcol < V) ? 1.f : 0.f;
+  } else if (p.init) {
     if (p.svec) {
 #pragma unroll
       for (int ct = 0; ct < C::KT; ++ct) {
@@ -345,6 +352,9 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
   // or the key/value range are zeroed in phase 0.
   using Raw = RawChunk<RPW, CPL, VPL, kBF16>;
   Raw raw;
+  // (with zero values v is never dereferenced: loads of v read k's rows instead)
+  const void* const vsrc = p.v_zero ? p.k : p.v;
+  const int64_t vstride = p.v_zero ? K : V;
   auto issue_loads = [&](int64_t tb) {
     const int64_t span = (len - tb) < (int64_t)kC ? (len - tb) : (int64_t)kC;
     int64_t th[RPW];
@@ -369,7 +379,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
         if (kBF16) {
           const unsigned short* k16 = static_cast<const unsigned short*>(p.k) + th[r] * K + cs;
           const unsigned short* q16 = static_cast<const unsigned short*>(p.q) + th[r] * K + cs;
-          const unsigned short* v16 = static_cast<const unsigned short*>(p.v) + th[r] * V + vs;
+          const unsigned short* v16 = static_cast<const unsigned short*>(vsrc) + th[r] * vstride + vs;
           if (CPL == 2) {
             raw.k[r][0] = *reinterpret_cast<const unsigned*>(k16);
             raw.q[r][0] = *reinterpret_cast<const unsigned*>(q16);
@@ -384,7 +394,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
         } else {
           const unsigned* k32 = static_cast<const unsigned*>(p.k) + th[r] * K + cs;
           const unsigned* q32 = static_cast<const unsigned*>(p.q) + th[r] * K + cs;
-          const unsigned* v32 = static_cast<const unsigned*>(p.v) + th[r] * V + vs;
+          const unsigned* v32 = static_cast<const unsigned*>(vsrc) + th[r] * vstride + vs;
           if (CPL == 2) {
             const uint2 a = *reinterpret_cast<const uint2*>(k32), c = *reinterpret_cast<const uint2*>(q32);
             raw.k[r][0] = a.x; raw.k[r][CPL - 1] = a.y;
@@ -426,8 +436,8 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
 #pragma unroll
         for (int vv = 0; vv < VPL; ++vv) {
           const int64_t vs = vc_lo + vv < V ? vc_lo + vv : V - 1;
-          vv2[vv] = kBF16 ? (unsigned)static_cast<const unsigned short*>(p.v)[th[r] * V + vs]
-                          : static_cast<const unsigned*>(p.v)[th[r] * V + vs];
+          vv2[vv] = kBF16 ? (unsigned)static_cast<const unsigned short*>(vsrc)[th[r] * vstride + vs]
+                          : static_cast<const unsigned*>(vsrc)[th[r] * vstride + vs];
         }
         if (kBF16 && CPL == 2) {
           raw.k[r][0] = kk[0] | (kk[CPL - 1] << 16);
@@ -502,7 +512,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
           x = __uint_as_float(raw.v[r][vv] << 16);
         else
           x = __uint_as_float(raw.v[r][vv]);
-        vx[r][vv] = (okr && vc_lo + vv < V) ? x : 0.f;
+        vx[r][vv] = (okr && vc_lo + vv < V && !p.v_zero) ? x : 0.f;
       }
     }
     // (beta V)^T: this lane's RPW consecutive rows of each of its value columns
@@ -815,7 +825,9 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
         S[ct] = mfma(ld_perm(sKB + (16 * ct + lr) * C::LDT + 32 * q2 + 4 * lg), bV[q2], S[ct]);
 
     // ---------------- output rows of this chunk ---------------------------
-    if (kBF16 && p.ovec) {
+    if (p.out == nullptr) {
+      // maps of a segment only (no outputs)
+    } else if (kBF16 && p.ovec) {
       // stage through LDS (KR is dead) and store whole 16-byte runs of rows
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
@@ -884,6 +896,125 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
 
 constexpr int64_t kPlanMaxN = 2048;
 
+// ---------------------------------------------------------------------------
+// Segment-parallel prefill of long sequences.  When a batch has too few
+// (sequence, head) chains to fill the GPU, every sequence is cut into
+// segments of seg_len tokens.  A segment acts on the state as an affine map
+// F(S) = M S + b (maps compose in order; the composition is associative):
+//   pass 1a: every segment from a zero state          -> b (its final state)
+//   pass 1b: every segment from the identity, with zero values -> M
+//   scan   : S_in(first) = initial, S_in(next) = M S_in + b, final state
+//   pass 2 : every segment again from its S_in        -> outputs
+// All segments of all sequences run in parallel in passes 1 and 2.
+// ---------------------------------------------------------------------------
+
+// Segment table: scu[0..nmax] token offsets of the segments (entries past the
+// last real segment are T, i.e. empty segments); sfirst[n] is the first
+// segment of sequence n, sfirst[N] the number of real segments.
+__global__ __launch_bounds__(1024) void seg_plan_kernel(const int32_t* __restrict__ cu, int64_t N, int64_t T,
+                                                        int64_t seg_len, int64_t nmax, int32_t* __restrict__ scu,
+                                                        int32_t* __restrict__ sfirst) {
+  __shared__ int32_t cnt[1025], first[1025];
+  for (int64_t n = threadIdx.x; n < N; n += blockDim.x) {
+    int64_t b0 = cu[n], e0 = cu[n + 1];
+    b0 = b0 < 0 ? 0 : (b0 > T ? T : b0);
+    e0 = e0 < b0 ? b0 : (e0 > T ? T : e0);
+    cnt[n] = (int32_t)((e0 - b0 + seg_len - 1) / seg_len);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    // prefix sums, clamped to nmax so that offsets that break the cu_seqlens
+    // precondition still cannot index past the workspace
+    int64_t run = 0;
+    for (int64_t n = 0; n < N; ++n) {
+      first[n] = (int32_t)run;
+      run = run + cnt[n] < nmax ? run + cnt[n] : nmax;
+    }
+    first[N] = (int32_t)run;
+  }
+  __syncthreads();
+  for (int64_t n = threadIdx.x; n <= N; n += blockDim.x) sfirst[n] = first[n];
+  for (int64_t n = threadIdx.x; n < N; n += blockDim.x) {
+    int64_t b0 = cu[n], e0 = cu[n + 1];
+    b0 = b0 < 0 ? 0 : (b0 > T ? T : b0);
+    e0 = e0 < b0 ? b0 : (e0 > T ? T : e0);
+    for (int64_t j = 0; first[n] + j < first[n + 1]; ++j) scu[first[n] + j] = (int32_t)(b0 + j * seg_len);
+  }
+  for (int64_t s = first[N] + threadIdx.x; s <= nmax; s += blockDim.x) scu[s] = (int32_t)T;
+}
+
+// Composes the segment maps of one (sequence, head) in fp32 (one workgroup of
+// 256 threads; K, V <= 128).  Writes each segment's initial state S_in
+// ([nmax, H, V, K] fp32) and the sequence's final state.
+__global__ __launch_bounds__(256) void seg_scan_kernel(const int32_t* __restrict__ sfirst, const float* __restrict__ bmap,
+                                                       const float* __restrict__ mmap, const void* __restrict__ init,
+                                                       int init_bf16, void* __restrict__ fin, int fin_bf16,
+                                                       float* __restrict__ sin, int64_t H, int64_t K, int64_t V) {
+  __shared__ float sS[128 * 129];  // S[c][v]
+  __shared__ float sM[128 * 129];  // M[c][c']
+  const int64_t n = blockIdx.x / H, h = blockIdx.x % H;
+  const int tid = threadIdx.x;
+  const int64_t srow = (n * H + h) * V;  // [.., H, V, K] row base of (n, h)
+  for (int e = tid; e < 128 * 128; e += 256) {
+    const int c = e & 127, v = e >> 7;
+    float x = 0.f;
+    if (init && c < K && v < V) {
+      const int64_t o = (srow + v) * K + c;
+      x = init_bf16 ? bf2f(static_cast<const unsigned short*>(init)[o]) : static_cast<const float*>(init)[o];
+    }
+    sS[c * 129 + v] = x;
+  }
+  __syncthreads();
+  const int r0 = 8 * (tid >> 4), c0 = 8 * (tid & 15);  // this thread's 8x8 block of S[c][v]
+  for (int64_t sg = sfirst[n]; sg < sfirst[n + 1]; ++sg) {
+    const int64_t srow_s = (sg * H + h) * V;
+    const int64_t mrow_s = (sg * H + h) * K;
+    for (int e = tid; e < 128 * 128; e += 256) {
+      const int c = e & 127, x = e >> 7;  // element (x, c) of the map tensor = M[c][x]
+      if (x < V && c < K) sin[(srow_s + x) * K + c] = sS[c * 129 + x];
+      sM[c * 129 + x] = (c < K && x < K) ? mmap[(mrow_s + x) * K + c] : 0.f;
+    }
+    __syncthreads();
+    float acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int c = r0 + i, v = c0 + j;
+        acc[i][j] = (c < K && v < V) ? bmap[(srow_s + v) * K + c] : 0.f;
+      }
+    for (int cp = 0; cp < K; ++cp) {
+      float mv[8], sv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mv[i] = sM[(r0 + i) * 129 + cp];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sv[j] = sS[cp * 129 + c0 + j];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] += mv[i] * sv[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sS[(r0 + i) * 129 + c0 + j] = acc[i][j];
+    __syncthreads();
+  }
+  if (fin) {
+    for (int e = tid; e < 128 * 128; e += 256) {
+      const int c = e & 127, v = e >> 7;
+      if (c < K && v < V) {
+        const int64_t o = (srow + v) * K + c;
+        if (fin_bf16)
+          static_cast<__bf16*>(fin)[o] = (__bf16)sS[c * 129 + v];
+        else
+          static_cast<float*>(fin)[o] = sS[c * 129 + v];
+      }
+    }
+  }
+}
+
 template <int KP, int BV>
 hipError_t launch_cfg(const Params& prm, bool bf16, hipStream_t stream) {
   const int64_t items = prm.N * prm.H;
@@ -897,15 +1028,64 @@ hipError_t launch_cfg(const Params& prm, bool bf16, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Picks the kernel variant for these sizes and launches it.
+hipError_t launch_variant(Params prm, bool bf16, hipStream_t stream, bool wide = false) {
+  const uintptr_t al = (uintptr_t)prm.q | (uintptr_t)prm.k | (uintptr_t)(prm.v_zero ? prm.k : prm.v) | (uintptr_t)prm.g;
+  prm.pair = (prm.K % 2 == 0) && (prm.V % 2 == 0) && (al % 8 == 0);
+  prm.ovec = (prm.V % 8 == 0) && ((uintptr_t)prm.out % 16 == 0);
+  const uintptr_t sal = (prm.init_identity ? 0 : (uintptr_t)prm.init) | (uintptr_t)prm.fin;
+  prm.svec = (prm.K % 4 == 0) && (sal % 16 == 0);
+  const int64_t chains = prm.N * prm.H;
+  // Few (sequence, head) chains: narrower value blocks give more workgroups.
+  if (prm.K <= 64) {
+    prm.nvb = (int)((prm.V + 63) / 64);
+    return launch_cfg<64, 64>(prm, bf16, stream);
+  }
+  // (wide: the segment passes size their chain count to one workgroup per CU)
+  if (prm.V <= 64 || (chains < 512 && !wide)) {
+    prm.nvb = (int)((prm.V + 63) / 64);
+    return launch_cfg<128, 64>(prm, bf16, stream);
+  }
+  prm.nvb = (int)((prm.V + 127) / 128);
+  return launch_cfg<128, 128>(prm, bf16, stream);
+}
+
+// Segment length when a batch is cut into segments, 0 when it is not.
+int64_t segment_length(int64_t T, int64_t N, int64_t H, int64_t K, int64_t V) {
+  if (N * H >= 256 || T < 16384 || K > 128 || V > 128 || N > 1024) return 0;
+  int64_t ls = (T * H + 255) / 256;  // about one chain per CU
+  ls = (ls + 63) / 64 * 64;
+  return ls < 2048 ? 2048 : ls;
+}
+
+struct SegLayout {
+  int64_t seg_len = 0, nmax = 0;
+  size_t off_scu = 0, off_sfirst = 0, off_b = 0, off_m = 0, off_sin = 0, total = 0;
+};
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+SegLayout seg_layout(int64_t T, int64_t N, int64_t H, int64_t K, int64_t V) {
+  SegLayout L;
+  L.seg_len = segment_length(T, N, H, K, V);
+  if (!L.seg_len) return L;
+  L.nmax = N + T / L.seg_len;
+  size_t o = 0;
+  L.off_scu = o;     o += round256(sizeof(int32_t) * (size_t)(L.nmax + 1));
+  L.off_sfirst = o;  o += round256(sizeof(int32_t) * (size_t)(N + 1));
+  L.off_b = o;       o += round256(sizeof(float) * (size_t)(L.nmax * H * V * K));
+  L.off_m = o;       o += round256(sizeof(float) * (size_t)(L.nmax * H * K * K));
+  L.off_sin = o;     o += round256(sizeof(float) * (size_t)(L.nmax * H * V * K));
+  L.total = o;
+  return L;
+}
 }  // namespace
 
 size_t chunk_prefill_workspace_bytes(int64_t T, int64_t N, int64_t H, int64_t K, int64_t V) {
-  (void)T;
-  (void)H;
-  (void)K;
-  (void)V;
+  const SegLayout L = seg_layout(T, N, H, K, V);
+  if (L.seg_len) return L.total;
   if (N < 2 || N > kPlanMaxN) return 0;
-  return (size_t)(((N * 4) + 255) / 256 * 256);
+  return round256((size_t)N * 4);
 }
 
 hipError_t launch_chunk_prefill(const kda_prefill_args_t& a, hipStream_t stream) {
@@ -930,31 +1110,59 @@ hipError_t launch_chunk_prefill(const kda_prefill_args_t& a, hipStream_t stream)
   prm.fin_bf16 = a.final_dtype == KDA_BF16;
   prm.l2norm = a.use_qk_l2norm != 0;
   prm.order = nullptr;
-  const uintptr_t al = (uintptr_t)a.q | (uintptr_t)a.k | (uintptr_t)a.v | (uintptr_t)a.g;
-  prm.pair = (a.K % 2 == 0) && (a.V % 2 == 0) && (al % 8 == 0);
-  prm.ovec = (a.V % 8 == 0) && ((uintptr_t)a.out % 16 == 0);
-  const uintptr_t sal = (uintptr_t)a.initial_state | (uintptr_t)a.final_state;
-  prm.svec = (a.K % 4 == 0) && (sal % 16 == 0);
+  prm.v_zero = 0;
+  prm.init_identity = 0;
+  prm.nvb = 1;
+  const bool bf16 = a.qkv_dtype == KDA_BF16;
+  hipError_t e;
+
+  const SegLayout L = seg_layout(a.T, a.N, a.H, a.K, a.V);
+  if (L.seg_len) {
+    char* ws = static_cast<char*>(a.workspace);
+    int32_t* scu = reinterpret_cast<int32_t*>(ws + L.off_scu);
+    int32_t* sfirst = reinterpret_cast<int32_t*>(ws + L.off_sfirst);
+    float* bmap = reinterpret_cast<float*>(ws + L.off_b);
+    float* mmap = reinterpret_cast<float*>(ws + L.off_m);
+    float* sin = reinterpret_cast<float*>(ws + L.off_sin);
+    hipLaunchKernelGGL(seg_plan_kernel, dim3(1), dim3(1024), 0, stream, a.cu_seqlens, a.N, a.T, L.seg_len, L.nmax,
+                       scu, sfirst);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    Params seg = prm;
+    seg.cu = scu;
+    seg.N = L.nmax;
+    // pass 1a: b of every segment
+    Params p1 = seg;
+    p1.init = nullptr;
+    p1.out = nullptr;
+    p1.fin = bmap;
+    p1.fin_bf16 = 0;
+    if ((e = launch_variant(p1, bf16, stream, true)) != hipSuccess) return e;
+    // pass 1b: M of every segment (identity state, zero values, V = K)
+    Params p2 = p1;
+    p2.V = a.K;
+    p2.v_zero = 1;
+    p2.init_identity = 1;
+    p2.fin = mmap;
+    if ((e = launch_variant(p2, bf16, stream, true)) != hipSuccess) return e;
+    // scan: S_in of every segment, final states
+    hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)(a.N * a.H)), dim3(256), 0, stream, sfirst, bmap, mmap,
+                       a.initial_state, prm.init_bf16, a.final_state, prm.fin_bf16, sin, a.H, a.K, a.V);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // pass 2: outputs of every segment from its true initial state
+    Params p3 = seg;
+    p3.init = sin;
+    p3.init_bf16 = 0;
+    p3.fin = nullptr;
+    return launch_variant(p3, bf16, stream, true);
+  }
+
   if (a.N >= 2 && a.N <= kPlanMaxN) {
     int32_t* order = static_cast<int32_t*>(a.workspace);
     hipLaunchKernelGGL(plan_order_kernel, dim3(1), dim3(1024), 0, stream, a.cu_seqlens, a.N, a.T, order);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     prm.order = order;
   }
-  const bool bf16 = a.qkv_dtype == KDA_BF16;
-  // Few (sequence, head) chains: narrower value blocks give more workgroups.
-  const int64_t chains = a.N * a.H;
-  if (a.K <= 64) {
-    prm.nvb = (int)((a.V + 63) / 64);
-    return launch_cfg<64, 64>(prm, bf16, stream);
-  }
-  if (a.V <= 64 || chains < 512) {
-    prm.nvb = (int)((a.V + 63) / 64);
-    return launch_cfg<128, 64>(prm, bf16, stream);
-  }
-  prm.nvb = (int)((a.V + 127) / 128);
-  return launch_cfg<128, 128>(prm, bf16, stream);
+  return launch_variant(prm, bf16, stream);
 }
 
 }  // namespace kda

@@ -148,3 +148,18 @@ def test_deterministic():
     o1, f1 = _run(inp)
     o2, f2 = _run(inp)
     assert np.array_equal(o1, o2) and np.array_equal(f1, f2)
+
+
+# --- segment-parallel path: few (sequence, head) chains and T >= 16384 ----------------
+@pytest.mark.parametrize("lengths,H,K,V,dtype,init", [
+    ([20000], 2, 64, 64, "bf16", False),
+    ([17000, 100, 0], 4, 128, 128, "bf16", True),
+    ([9000, 9001], 3, 32, 48, "f32", True),
+])
+def test_segmented_long_sequences(lengths, H, K, V, dtype, init):
+    import kda_recurrent_state_amd as kda
+    T = sum(lengths)
+    assert len(lengths) * H < 256 and T >= 16384
+    assert kda.kda_chunk_prefill_workspace_size(T, len(lengths), H, K, V) > 0   # segmentation is on
+    inp = wl.host_prefill_inputs(lengths, H, K, V, dtype=dtype, seed=T + H, initial=init)
+    _check(inp, final_dtype="bf16" if init else "f32")
