@@ -230,6 +230,70 @@ def bench_other(args, dev):
     return base
 
 
+def bench_ckpt(args, dev, interval: int = 1024):
+    """The e2e step with prefill checkpoints: every 1024 tokens of each
+    sequence the state is written (bf16) and then scattered into free cache
+    rows, next to the final states."""
+    import torch
+    import kda_recurrent_state_amd as kda
+    w = build_workload(args.seed, dev)
+    inp, N = w["inp"], w["N"]
+    T = int(inp["T"])
+    offs = kda.checkpoint_offsets(w["lengths"], interval)
+    n_ck = offs[-1]
+    used = set(int(x) for x in w["sidx_np"].tolist())
+    free = [r for r in range(NUM_ROWS) if r not in used][:n_ck]
+    assert len(free) == n_ck
+    ck_idx = torch.tensor(free, dtype=torch.int32, device=dev)
+    ck_cu = torch.tensor(offs, dtype=torch.int32, device=dev)
+    ck = torch.empty((max(n_ck, 1), H, V, K), dtype=torch.bfloat16, device=dev)
+    pin, pout = w["packed_in"][:N], w["packed_out"][:N]
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        kda.kda_state_gather(w["cache"], w["gidx"], w["flags"], pin)
+        if ev is not None:
+            ev[1].record(stream)
+        kda.kda_chunk_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["cu_seqlens"],
+                              initial_state=pin, out=w["out"], final_state=pout, workspace=w["ws"],
+                              ckpt_interval=interval, ckpt_cu=ck_cu, ckpt_states=ck[:n_ck])
+        if ev is not None:
+            ev[2].record(stream)
+        kda.kda_state_scatter(w["cache"], w["sidx"], pout)
+        kda.kda_state_scatter(w["cache"], ck_idx, ck[:n_ck])
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    c_avg = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    s_avg = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    ck_bytes = n_ck * H * V * K * 2
+    nbytes = chunk_bytes_per_launch(T, N) + ck_bytes
+    return {"metric": METRIC, "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "e2e prefill step with checkpoints: the e2e step plus the state after every "
+                                   "%d tokens of each sequence (%d checkpoints, bf16) scattered into free cache rows"
+                                   % (interval, n_ck),
+                       "global_batch": N, "seq_len": T, "tokens": T, "checkpoints": n_ck, "seed": args.seed},
+            "roofline": {"bound": "hbm", "achieved": nbytes / (c_avg * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": nbytes / (c_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, "traffic": None,
+                         "kernel": "kda_chunk_prefill (with checkpoints)", "algorithmic_bytes_per_launch": nbytes,
+                         "avg_launch_ms": c_avg},
+            "stages_ms": {"chunk_prefill": c_avg, "scatter_final_and_checkpoints": s_avg},
+            "checkpoint_bytes": ck_bytes}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -239,10 +303,11 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true", help="run only a plain 1 GiB device copy")
-    ap.add_argument("--workload", default="e2e", choices=["e2e", "varlen", "long", "copy"],
+    ap.add_argument("--workload", default="e2e", choices=["e2e", "varlen", "long", "copy", "ckpt"],
                     help="e2e (default, the headline step); varlen / long: the chunk prefill on 16 sequences of "
                          "512-4096 tokens / one 65536-token sequence (state gathered from and scattered to a bf16 "
-                         "cache for long); copy: state gather/scatter on an fp32 [1024,32,128,128] cache")
+                         "cache for long); copy: state gather/scatter on an fp32 [1024,32,128,128] cache; ckpt: "
+                         "the e2e step plus checkpoints every 1024 tokens scattered into cache rows")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -263,6 +328,9 @@ def main():
         calibrate_copy(dev)
         return
 
+    if args.workload == "ckpt":
+        print(json.dumps(bench_ckpt(args, dev)))
+        return
     if args.workload != "e2e":
         print(json.dumps(bench_other(args, dev)))
         return

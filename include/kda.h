@@ -171,6 +171,28 @@ typedef struct {
   int use_qk_l2norm;
   void* workspace;
   size_t workspace_bytes;
+  /* Optional chunk-boundary checkpoints (prefix states that a cache can keep
+   * and later resume from; [P2] section 1.3 and section 5.2's checkpoints at
+   * chunk boundaries).  With ckpt_states != NULL, for sequence n the j-th
+   * checkpoint (j = 0 .. ckpt_cu[n+1]-ckpt_cu[n]-1) is the state after
+   * (j+1)*ckpt_interval tokens of that sequence, written to row ckpt_cu[n]+j
+   * of ckpt_states ([num_ckpt, H, V, K], ckpt_dtype, same element order as
+   * final_state, rounded like final_state).  Positions past the sequence's
+   * length and rows outside [0, num_ckpt) are not written; the natural
+   * choice is ckpt_cu[n+1]-ckpt_cu[n] = floor(len_n / ckpt_interval).
+   * Chunks never straddle a multiple of 64 tokens of a sequence, so the
+   * checkpoint states are exact chunk-boundary states, and requesting them
+   * does not change out or final_state.
+   *  ckpt_interval -- positive multiple of 64 (ignored when ckpt_states is NULL).
+   *  ckpt_cu       -- [N+1] int32 device array of checkpoint row offsets,
+   *                   non-decreasing (not checked).
+   *  ckpt_states   -- device output, num_ckpt rows, or NULL for none.  It must
+   *                   not overlap any other argument (not checked). */
+  int64_t ckpt_interval;
+  const int32_t* ckpt_cu;
+  void* ckpt_states;
+  int64_t num_ckpt;
+  kda_dtype_t ckpt_dtype;
 } kda_prefill_args_t;
 
 /* Bytes of device workspace kda_chunk_prefill needs for these sizes. */

@@ -10,8 +10,8 @@ The library must be built (``python -m kda_recurrent_state_amd.build``); there
 is no fallback implementation.
 """
 from ._lib import KDAError, load_library  # noqa: F401
-from .api import (KDAStateCopy, cache_descriptor, kda_chunk_prefill,  # noqa: F401
+from .api import (KDAStateCopy, cache_descriptor, checkpoint_offsets, kda_chunk_prefill,  # noqa: F401
                   kda_chunk_prefill_workspace_size, kda_state_gather, kda_state_scatter)
 
 __all__ = ["kda_state_gather", "kda_state_scatter", "kda_chunk_prefill", "kda_chunk_prefill_workspace_size",
-           "KDAStateCopy", "KDAError", "load_library", "cache_descriptor"]
+           "KDAStateCopy", "KDAError", "load_library", "cache_descriptor", "checkpoint_offsets"]

@@ -33,7 +33,9 @@ class PrefillArgs(ctypes.Structure):
                 ("out", ctypes.c_void_p),
                 ("final_state", ctypes.c_void_p), ("final_dtype", ctypes.c_int),
                 ("scale", ctypes.c_float), ("use_qk_l2norm", ctypes.c_int),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("ckpt_interval", ctypes.c_int64), ("ckpt_cu", ctypes.c_void_p), ("ckpt_states", ctypes.c_void_p),
+                ("num_ckpt", ctypes.c_int64), ("ckpt_dtype", ctypes.c_int)]
 
 
 class KDAError(RuntimeError):

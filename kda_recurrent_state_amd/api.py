@@ -104,16 +104,23 @@ def kda_chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torc
                       cu_seqlens: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
                       out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
                       final_dtype: Optional[torch.dtype] = torch.float32, scale: Optional[float] = None,
-                      use_qk_l2norm: bool = True, workspace: Optional[torch.Tensor] = None, stream=None):
+                      use_qk_l2norm: bool = True, workspace: Optional[torch.Tensor] = None, stream=None,
+                      ckpt_interval: int = 0, ckpt_cu: Optional[torch.Tensor] = None,
+                      ckpt_states: Optional[torch.Tensor] = None):
     """Chunked gated delta rule over a varlen batch.
 
     q, k: [T,H,K]; v: [T,H,V] (fp32 or bf16, same dtype); g: [T,H,K] fp32;
     beta: [T,H]; cu_seqlens: [N+1] int32; initial_state: [N,H,V,K] or None.
     Returns (out [T,H,V], final_state [N,H,V,K] or None).  ``out`` may be ``v``.
     ``final_dtype=None`` skips the final state unless ``final_state`` is given.
+
+    Checkpoints (optional): with ``ckpt_states`` ([num_ckpt,H,V,K], fp32 or
+    bf16) and ``ckpt_cu`` ([N+1] int32, e.g. from ``checkpoint_offsets``),
+    row ckpt_cu[n]+j receives the state of sequence n after
+    (j+1)*ckpt_interval tokens; ckpt_interval is a positive multiple of 64.
     """
     lib = _lib.load_library()
-    _require_cuda(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, workspace)
+    _require_cuda(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, workspace, ckpt_cu, ckpt_states)
     if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
         raise KDAError("kda_chunk_prefill", 3, "q,k must be [T,H,K] and v [T,H,V]")
     T, H, K = (int(x) for x in q.shape)
@@ -139,6 +146,11 @@ def kda_chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torc
     for name, s in (("initial_state", initial_state), ("final_state", final_state)):
         if s is not None and (tuple(s.shape) != (N, H, V, K) or not s.is_contiguous()):
             raise KDAError("kda_chunk_prefill", 3, "%s must be a contiguous [N,H,V,K] tensor" % name)
+    if ckpt_states is not None:
+        if ckpt_cu is None or ckpt_cu.dtype != torch.int32 or ckpt_cu.numel() != N + 1:
+            raise KDAError("kda_chunk_prefill", 2, "ckpt_cu must be int32 [N+1]")
+        if ckpt_states.dim() != 4 or tuple(ckpt_states.shape[1:]) != (H, V, K) or not ckpt_states.is_contiguous():
+            raise KDAError("kda_chunk_prefill", 3, "ckpt_states must be a contiguous [num_ckpt,H,V,K] tensor")
     need = int(lib.kda_chunk_prefill_workspace_size(T, N, H, K, V))
     if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -159,9 +171,26 @@ def kda_chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torc
     a.use_qk_l2norm = 1 if use_qk_l2norm else 0
     a.workspace = workspace.data_ptr() if (workspace is not None and need > 0) else None
     a.workspace_bytes = need if (workspace is not None and need > 0) else 0
+    if ckpt_states is not None:
+        a.ckpt_interval = int(ckpt_interval)
+        a.ckpt_cu = ckpt_cu.data_ptr()
+        a.ckpt_states = ckpt_states.data_ptr()
+        a.num_ckpt = int(ckpt_states.shape[0])
+        a.ckpt_dtype = _dtype_code(ckpt_states, "kda_chunk_prefill")
     st = lib.kda_chunk_prefill(ctypes.byref(a), _stream_handle(stream))
     _lib.check("kda_chunk_prefill", st)
     return out, final_state
+
+
+def checkpoint_offsets(lengths, interval: int):
+    """Row offsets [N+1] of the chunk-boundary checkpoints of a batch: sequence
+    n of length len_n owns floor(len_n / interval) rows (host-side helper)."""
+    if interval <= 0 or interval % 64:
+        raise ValueError("interval must be a positive multiple of 64")
+    offs = [0]
+    for n in lengths:
+        offs.append(offs[-1] + int(n) // int(interval))
+    return offs
 
 
 class KDAStateCopy:

@@ -234,6 +234,17 @@ struct Params {
   int svec;              // K % 4 == 0 and state pointers aligned: vector state I/O
   int v_zero;            // values are all zero (v is not read)
   int init_identity;     // initial state is the identity (K == V); init is not read
+  // chunk-boundary checkpoints: the state after every ckpt_iv tokens of a
+  // sequence goes to row ckpt_cu[seq] + j of ckpt (rows outside [0, num_ckpt)
+  // are skipped)
+  void* ckpt;            // NULL: none
+  const int32_t* ckpt_cu;
+  int64_t ckpt_iv, num_ckpt;
+  int ckpt_bf16;
+  // segments: seq_of[n] is the sequence that work item n belongs to and
+  // seq_cu the sequences' token offsets (NULL: items are whole sequences)
+  const int32_t* seq_of;
+  const int32_t* seq_cu;
 };
 
 // Raw bits of one chunk's inputs as loaded (bf16 pairs packed in one word),
@@ -245,6 +256,40 @@ struct RawChunk {
   unsigned k[RPW][KW], q[RPW][KW], v[RPW][VW], b[RPW];
   float g[RPW][CPL];
 };
+
+// Writes one lane's state columns (MFMA C layout, S[ct][e] = S(16ct + 4kg + e,
+// vc)) to rows [row, row + V) of a [.., V, K] state array.
+template <int KT>
+__device__ __forceinline__ void store_state(const f32x4 (&S)[KT], void* dst, int bf, int svec, int64_t row, int kg,
+                                            int64_t vc, int64_t K, int64_t V) {
+  if (vc >= V) return;
+  if (svec) {
+#pragma unroll
+    for (int ct = 0; ct < KT; ++ct) {
+      const int64_t c0 = 16 * ct + 4 * kg;
+      if (c0 >= K) continue;
+      const int64_t o = (row + vc) * K + c0;
+      if (bf)
+        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(dst) + o) =
+            bf16x4{(__bf16)S[ct][0], (__bf16)S[ct][1], (__bf16)S[ct][2], (__bf16)S[ct][3]};
+      else
+        *reinterpret_cast<f32x4*>(static_cast<float*>(dst) + o) = S[ct];
+    }
+  } else {
+#pragma unroll
+    for (int ct = 0; ct < KT; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t c = 16 * ct + 4 * kg + e;
+        if (c >= K) continue;
+        const int64_t o = (row + vc) * K + c;
+        if (bf)
+          static_cast<__bf16*>(dst)[o] = (__bf16)S[ct][e];
+        else
+          static_cast<float*>(dst)[o] = S[ct][e];
+      }
+  }
+}
 
 template <int KP, int BV, bool kBF16>
 __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
@@ -459,11 +504,33 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     }
   };
 
+  // Checkpoints: ck_next is the next checkpoint position relative to bos and
+  // ck_row its row (both uniform).  Chunks never straddle a multiple of 64
+  // tokens and ckpt_iv is a multiple of 64, so every checkpoint position is
+  // a chunk end.
+  int64_t ck_next = INT64_MAX, ck_row = 0, ck_end = 0;
+  if (p.ckpt) {
+    int64_t seq = n, off = 0;
+    if (p.seq_of) {
+      seq = p.seq_of[n];
+      int64_t sb = p.seq_cu[seq];
+      sb = sb < 0 ? 0 : (sb > p.T ? p.T : sb);
+      off = bos - sb;
+    }
+    const int64_t j = off / p.ckpt_iv;  // checkpoints that end at or before this item's start
+    ck_next = (j + 1) * p.ckpt_iv - off;
+    ck_row = (int64_t)p.ckpt_cu[seq] + j;
+    ck_end = p.ckpt_cu[seq + 1];
+    ck_end = ck_end < p.num_ckpt ? ck_end : p.num_ckpt;
+  }
+
   int64_t t0 = 0;
   int Lcap = kC;
   if (len > 0) issue_loads(0);
   while (t0 < len) {
-    const int L = (int)((len - t0) < (int64_t)Lcap ? (len - t0) : (int64_t)Lcap);
+    // chunk length: the cap, the tokens left, and the next multiple of 64
+    int L = (int)((len - t0) < (int64_t)Lcap ? (len - t0) : (int64_t)Lcap);
+    L = L < kC - (int)(t0 & (kC - 1)) ? L : kC - (int)(t0 & (kC - 1));
     lds_barrier();  // the previous chunk's LDS readers are done
     // Per-iteration copies of the lane indices, opaque to the optimiser: this
     // keeps every lane-dependent LDS address from being hoisted out of the
@@ -861,37 +928,20 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     }
     t0 += L;
     Lcap = kC;
+    if (t0 == ck_next) {
+      if (ck_row >= 0 && ck_row < ck_end) {
+        int tid_c = tid;
+        asm volatile("" : "+v"(tid_c));
+        store_state(S, p.ckpt, p.ckpt_bf16, p.svec, (ck_row * H + h) * V, (tid_c & 63) >> 4, v0 + 16 * w + (tid_c & 15),
+                    K, V);
+      }
+      ck_next += p.ckpt_iv;
+      ++ck_row;
+    }
   }
 
   // ---- final state ----
-  if (p.fin && vcol < V) {
-    if (p.svec) {
-#pragma unroll
-      for (int ct = 0; ct < C::KT; ++ct) {
-        const int64_t c0 = 16 * ct + 4 * lg;
-        if (c0 >= K) continue;
-        const int64_t o = (srow + vcol) * K + c0;
-        if (p.fin_bf16)
-          *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(p.fin) + o) =
-              bf16x4{(__bf16)S[ct][0], (__bf16)S[ct][1], (__bf16)S[ct][2], (__bf16)S[ct][3]};
-        else
-          *reinterpret_cast<f32x4*>(static_cast<float*>(p.fin) + o) = S[ct];
-      }
-    } else {
-#pragma unroll
-      for (int ct = 0; ct < C::KT; ++ct)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int64_t c = 16 * ct + 4 * lg + e;
-          if (c >= K) continue;
-          const int64_t o = (srow + vcol) * K + c;
-          if (p.fin_bf16)
-            static_cast<__bf16*>(p.fin)[o] = (__bf16)S[ct][e];
-          else
-            static_cast<float*>(p.fin)[o] = S[ct][e];
-        }
-    }
-  }
+  if (p.fin) store_state(S, p.fin, p.fin_bf16, p.svec, srow, lg, vcol, K, V);
 }
 
 constexpr int64_t kPlanMaxN = 2048;
@@ -910,10 +960,11 @@ constexpr int64_t kPlanMaxN = 2048;
 
 // Segment table: scu[0..nmax] token offsets of the segments (entries past the
 // last real segment are T, i.e. empty segments); sfirst[n] is the first
-// segment of sequence n, sfirst[N] the number of real segments.
+// segment of sequence n, sfirst[N] the number of real segments; sseq[s] is
+// the sequence of segment s (0 for the empty ones).
 __global__ __launch_bounds__(1024) void seg_plan_kernel(const int32_t* __restrict__ cu, int64_t N, int64_t T,
                                                         int64_t seg_len, int64_t nmax, int32_t* __restrict__ scu,
-                                                        int32_t* __restrict__ sfirst) {
+                                                        int32_t* __restrict__ sfirst, int32_t* __restrict__ sseq) {
   __shared__ int32_t cnt[1025], first[1025];
   for (int64_t n = threadIdx.x; n < N; n += blockDim.x) {
     int64_t b0 = cu[n], e0 = cu[n + 1];
@@ -938,9 +989,15 @@ __global__ __launch_bounds__(1024) void seg_plan_kernel(const int32_t* __restric
     int64_t b0 = cu[n], e0 = cu[n + 1];
     b0 = b0 < 0 ? 0 : (b0 > T ? T : b0);
     e0 = e0 < b0 ? b0 : (e0 > T ? T : e0);
-    for (int64_t j = 0; first[n] + j < first[n + 1]; ++j) scu[first[n] + j] = (int32_t)(b0 + j * seg_len);
+    for (int64_t j = 0; first[n] + j < first[n + 1]; ++j) {
+      scu[first[n] + j] = (int32_t)(b0 + j * seg_len);
+      sseq[first[n] + j] = (int32_t)n;
+    }
   }
-  for (int64_t s = first[N] + threadIdx.x; s <= nmax; s += blockDim.x) scu[s] = (int32_t)T;
+  for (int64_t s = first[N] + threadIdx.x; s <= nmax; s += blockDim.x) {
+    scu[s] = (int32_t)T;
+    if (s < nmax) sseq[s] = 0;
+  }
 }
 
 // Composes the segment maps of one (sequence, head) in fp32 (one workgroup of
@@ -1033,7 +1090,7 @@ hipError_t launch_variant(Params prm, bool bf16, hipStream_t stream, bool wide =
   const uintptr_t al = (uintptr_t)prm.q | (uintptr_t)prm.k | (uintptr_t)(prm.v_zero ? prm.k : prm.v) | (uintptr_t)prm.g;
   prm.pair = (prm.K % 2 == 0) && (prm.V % 2 == 0) && (al % 8 == 0);
   prm.ovec = (prm.V % 8 == 0) && ((uintptr_t)prm.out % 16 == 0);
-  const uintptr_t sal = (prm.init_identity ? 0 : (uintptr_t)prm.init) | (uintptr_t)prm.fin;
+  const uintptr_t sal = (prm.init_identity ? 0 : (uintptr_t)prm.init) | (uintptr_t)prm.fin | (uintptr_t)prm.ckpt;
   prm.svec = (prm.K % 4 == 0) && (sal % 16 == 0);
   const int64_t chains = prm.N * prm.H;
   // Few (sequence, head) chains: narrower value blocks give more workgroups.
@@ -1060,7 +1117,7 @@ int64_t segment_length(int64_t T, int64_t N, int64_t H, int64_t K, int64_t V) {
 
 struct SegLayout {
   int64_t seg_len = 0, nmax = 0;
-  size_t off_scu = 0, off_sfirst = 0, off_b = 0, off_m = 0, off_sin = 0, total = 0;
+  size_t off_scu = 0, off_sfirst = 0, off_sseq = 0, off_b = 0, off_m = 0, off_sin = 0, total = 0;
 };
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
@@ -1073,6 +1130,7 @@ SegLayout seg_layout(int64_t T, int64_t N, int64_t H, int64_t K, int64_t V) {
   size_t o = 0;
   L.off_scu = o;     o += round256(sizeof(int32_t) * (size_t)(L.nmax + 1));
   L.off_sfirst = o;  o += round256(sizeof(int32_t) * (size_t)(N + 1));
+  L.off_sseq = o;    o += round256(sizeof(int32_t) * (size_t)L.nmax);
   L.off_b = o;       o += round256(sizeof(float) * (size_t)(L.nmax * H * V * K));
   L.off_m = o;       o += round256(sizeof(float) * (size_t)(L.nmax * H * K * K));
   L.off_sin = o;     o += round256(sizeof(float) * (size_t)(L.nmax * H * V * K));
@@ -1113,6 +1171,13 @@ hipError_t launch_chunk_prefill(const kda_prefill_args_t& a, hipStream_t stream)
   prm.v_zero = 0;
   prm.init_identity = 0;
   prm.nvb = 1;
+  prm.ckpt = a.ckpt_states;
+  prm.ckpt_cu = a.ckpt_cu;
+  prm.ckpt_iv = a.ckpt_interval;
+  prm.num_ckpt = a.num_ckpt;
+  prm.ckpt_bf16 = a.ckpt_dtype == KDA_BF16;
+  prm.seq_of = nullptr;
+  prm.seq_cu = nullptr;
   const bool bf16 = a.qkv_dtype == KDA_BF16;
   hipError_t e;
 
@@ -1121,11 +1186,12 @@ hipError_t launch_chunk_prefill(const kda_prefill_args_t& a, hipStream_t stream)
     char* ws = static_cast<char*>(a.workspace);
     int32_t* scu = reinterpret_cast<int32_t*>(ws + L.off_scu);
     int32_t* sfirst = reinterpret_cast<int32_t*>(ws + L.off_sfirst);
+    int32_t* sseq = reinterpret_cast<int32_t*>(ws + L.off_sseq);
     float* bmap = reinterpret_cast<float*>(ws + L.off_b);
     float* mmap = reinterpret_cast<float*>(ws + L.off_m);
     float* sin = reinterpret_cast<float*>(ws + L.off_sin);
     hipLaunchKernelGGL(seg_plan_kernel, dim3(1), dim3(1024), 0, stream, a.cu_seqlens, a.N, a.T, L.seg_len, L.nmax,
-                       scu, sfirst);
+                       scu, sfirst, sseq);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     Params seg = prm;
     seg.cu = scu;
@@ -1134,6 +1200,7 @@ hipError_t launch_chunk_prefill(const kda_prefill_args_t& a, hipStream_t stream)
     Params p1 = seg;
     p1.init = nullptr;
     p1.out = nullptr;
+    p1.ckpt = nullptr;
     p1.fin = bmap;
     p1.fin_bf16 = 0;
     if ((e = launch_variant(p1, bf16, stream, true)) != hipSuccess) return e;
@@ -1153,6 +1220,8 @@ hipError_t launch_chunk_prefill(const kda_prefill_args_t& a, hipStream_t stream)
     p3.init = sin;
     p3.init_bf16 = 0;
     p3.fin = nullptr;
+    p3.seq_of = sseq;
+    p3.seq_cu = a.cu_seqlens;
     return launch_variant(p3, bf16, stream, true);
   }
 

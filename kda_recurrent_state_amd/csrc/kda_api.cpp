@@ -103,6 +103,11 @@ kda_status_t kda_chunk_prefill(const kda_prefill_args_t* a, void* stream) {
   if (a->initial_state && !valid_dtype(a->initial_dtype)) return KDA_E_DTYPE;
   if (a->final_state && !valid_dtype(a->final_dtype)) return KDA_E_DTYPE;
   if (a->K > 128) return KDA_E_UNSUPPORTED;
+  if (a->ckpt_states) {
+    if (a->ckpt_interval <= 0 || a->ckpt_interval % 64 != 0 || a->num_ckpt < 0) return KDA_E_SHAPE;
+    if (!a->ckpt_cu) return KDA_E_NULL;
+    if (!valid_dtype(a->ckpt_dtype)) return KDA_E_DTYPE;
+  }
   if (a->T > ((int64_t)1 << 40) / (a->H * (a->K > a->V ? a->K : a->V))) return KDA_E_SHAPE;
   if (a->N == 0) return KDA_OK;
   if (!a->cu_seqlens) return KDA_E_NULL;

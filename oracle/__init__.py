@@ -15,6 +15,8 @@ What it provides (fp64, plain loops in ``kda_oracle.c``):
   S_t = (I - beta_t k_t k_t^T) Diag(exp g_t) S_{t-1} + beta_t k_t v_t^T,
   o_t = scale * S_t^T q_t, over a varlen batch (page
   "【轻量化复刻大模型 / KIMI K3】KDA 对 AI Infra 的挑战与各家应对", section 1.1).
+* :func:`checkpoint_states` -- states at every ``interval`` tokens of each
+  sequence (prefix-boundary checkpoints), from the recurrence above.
 * :mod:`oracle.chunk_form` -- the same map evaluated through the chunk
   decomposition stages of "PR #33465 完整报告" (section "关键源码片段"), in
   fp64 numpy; used to pin the chunk formulas, never by the product path.
@@ -163,6 +165,44 @@ def kda_recurrence(q, k, v, g, beta, cu_seqlens, initial=None, scale=None, use_l
     if rc != 0:
         raise RuntimeError("oracle_kda_recurrence failed: %d" % rc)
     return out, fin
+
+
+def checkpoint_states(q, k, v, g, beta, cu_seqlens, interval, initial=None, scale=None, use_l2norm=True,
+                      eps=L2NORM_EPS, threads=1):
+    """States at prefix boundaries, in fp64: for sequence n (length len_n) and
+    j < floor(len_n / interval), row ckpt_offsets[n] + j is the state after
+    (j+1)*interval tokens of that sequence (the prefix-boundary checkpoint of
+    "【轻量化复刻大模型 / KIMI K3】KDA 对 AI Infra 的挑战与各家应对", section
+    1.3; section 5.2 places prefill checkpoints at chunk boundaries).
+
+    By definition such a state is the final state of the recurrence run over
+    the prefix alone.  It is computed here by running the recurrence over
+    consecutive ``interval``-token pieces, each resuming from the previous
+    piece's final state (the recurrence is one token at a time, so this is
+    the same arithmetic as one run over the prefix).
+    Returns (states [num_ckpt,H,V,K] float64, offsets list of N+1 ints).
+    """
+    cu = [int(x) for x in np.asarray(cu_seqlens).tolist()]
+    N = len(cu) - 1
+    T, H, K = np.shape(q)
+    V = np.shape(v)[2]
+    counts = [(cu[n + 1] - cu[n]) // int(interval) for n in range(N)]
+    offs = [0]
+    for c in counts:
+        offs.append(offs[-1] + c)
+    states = np.zeros((offs[-1], H, V, K), dtype=np.float64)
+    cur = np.zeros((N, H, V, K), dtype=np.float64) if initial is None else np.array(initial, dtype=np.float64)
+    for j in range(max(counts, default=0)):
+        sel = [n for n in range(N) if counts[n] > j]
+        rows = np.concatenate([np.arange(cu[n] + j * interval, cu[n] + (j + 1) * interval) for n in sel])
+        pcu = np.arange(len(sel) + 1, dtype=np.int64) * int(interval)
+        _, fin = kda_recurrence(np.asarray(q)[rows], np.asarray(k)[rows], np.asarray(v)[rows], np.asarray(g)[rows],
+                                np.asarray(beta)[rows], pcu, cur[sel], scale=scale, use_l2norm=use_l2norm, eps=eps,
+                                threads=threads)
+        for i, n in enumerate(sel):
+            cur[n] = fin[i]
+            states[offs[n] + j] = fin[i]
+    return states, offs
 
 
 def default_threads() -> int:

@@ -122,6 +122,11 @@ def _args(**kw):
     (dict(N=4, workspace=0, workspace_bytes=0), 7),
     (dict(out=0x3000 + 4), 8),                    # partial overlap with v
     (dict(out=0x1000), 8),                        # overlaps q
+    (dict(ckpt_states=0x9000, ckpt_cu=0xa000, ckpt_interval=100), 3),   # not a multiple of 64
+    (dict(ckpt_states=0x9000, ckpt_cu=0xa000, ckpt_interval=0), 3),
+    (dict(ckpt_states=0x9000, ckpt_cu=0xa000, ckpt_interval=64, num_ckpt=-1), 3),
+    (dict(ckpt_states=0x9000, ckpt_cu=0, ckpt_interval=64), 1),
+    (dict(ckpt_states=0x9000, ckpt_cu=0xa000, ckpt_interval=64, ckpt_dtype=5), 2),
 ])
 def test_prefill_rejections(lib, kw, status):
     a = _args(**kw)
@@ -131,6 +136,14 @@ def test_prefill_rejections(lib, kw, status):
 def test_prefill_empty_batch_is_ok(lib):
     a = _args(N=0, T=0)
     assert lib.kda_chunk_prefill(ctypes.byref(a), None) == 0
+
+
+def test_checkpoint_offsets_helper():
+    from kda_recurrent_state_amd.api import checkpoint_offsets
+    assert checkpoint_offsets([300, 64, 0, 63, 128], 64) == [0, 4, 5, 5, 5, 7]
+    assert checkpoint_offsets([1000], 192) == [0, 5]
+    with pytest.raises(ValueError):
+        checkpoint_offsets([10], 100)
 
 
 def test_workspace_size(lib):

@@ -314,3 +314,42 @@ def test_chunk_form_planted_mistake_is_caught():
     o1, f1 = oracle.kda_recurrence(q, k, v, g, b, cu, s0)
     o2, f2 = chunk_form.kda_chunked(q, k, v, np.zeros_like(g), b, cu, s0)
     assert _relerr(f2, f1) > 1e-2
+
+
+# -----------------------------------------------------------------------------
+def _explicit_state(q, k, v, g, b, t0, t1, h, S0_kv):
+    """State after tokens [t0, t1) of head h by the explicit product form."""
+    K = k.shape[2]
+    S = S0_kv.copy()
+    for t in range(t0, t1):
+        kh = _unit(k[t, h])
+        M = (np.eye(K) - b[t, h] * np.outer(kh, kh)) @ np.diag(np.exp(g[t, h]))
+        S = M @ S + b[t, h] * np.outer(kh, v[t, h])
+    return S
+
+
+@pytest.mark.parametrize("interval", [3, 4])
+def test_checkpoint_states_are_prefix_states(interval):
+    """Checkpoint j of sequence n is the state after (j+1)*interval of its tokens
+    (section 1.3's boundary state), checked against the explicit product form
+    and against one run over the prefix alone; rows follow floor(len/interval)."""
+    lengths = [7, 0, 4, 9, 2]
+    H, K, V = 2, 3, 2
+    q, k, v, g, b, cu, s0 = _rand_inputs(31, lengths, H, K, V)
+    states, offs = oracle.checkpoint_states(q, k, v, g, b, cu, interval, s0)
+    assert offs == list(np.cumsum([0] + [n // interval for n in lengths]))
+    assert states.shape == (offs[-1], H, V, K)
+    for n, ln in enumerate(lengths):
+        for j in range(ln // interval):
+            t1 = cu[n] + (j + 1) * interval
+            for h in range(H):
+                ref = _explicit_state(q, k, v, g, b, cu[n], t1, h, s0[n, h].T)
+                assert _relerr(states[offs[n] + j, h].T, ref) < 1e-12
+            sl = slice(cu[n], t1)
+            _, fin = oracle.kda_recurrence(q[sl], k[sl], v[sl], g[sl], b[sl], [0, t1 - cu[n]], s0[n:n + 1])
+            assert np.array_equal(states[offs[n] + j], fin[0])
+    # a length that is a multiple of the interval: the last checkpoint is the final state
+    _, fin = oracle.kda_recurrence(q, k, v, g, b, cu, s0)
+    n = lengths.index(max(lengths))
+    if lengths[n] % interval == 0:
+        assert np.array_equal(states[offs[n + 1] - 1], fin[n])
