@@ -187,6 +187,29 @@ def bench_other(args, dev):
                                   "kernel": "state_copy_kernel"},
                      "per_index_type": res})
         return base
+    if args.workload == "decode":
+        nseq, nrows = 512, NUM_ROWS
+        back, off, shape, strides = wl.device_cache(nrows, H, V, K, dtype="bf16", gap=wl.GAP, offset=0,
+                                                    seed=args.seed + 1, device=dev)
+        cache = torch.as_strided(back.view(torch.bfloat16), shape, strides, off)
+        inp = wl.device_prefill_inputs([1] * nseq, H, K, V, dtype="bf16", seed=args.seed, device=dev, initial=False)
+        idx = torch.from_numpy(wl.rng(args.seed + 2).permutation(nrows)[:nseq].astype(np.int32)).to(dev)
+        out = torch.empty_like(inp["v"])
+        fn = lambda: kda.kda_recurrent_decode(cache, idx, inp["q"], inp["k"], inp["v"], inp["g"],  # noqa: E731
+                                              inp["beta"], out=out)
+        nbytes = nseq * H * (2 * K * V * 2 + 2 * K + 2 * K + 2 * V + 4 * K + 4 + 2 * V) + 4 * nseq
+        ms_wall, ms_ev = _timed(fn, args.steps, args.warmup)
+        base.update({"metric": "KDA recurrent decode tokens/s (H=32,K=V=128), 1 GPU", "value": nseq / (ms_wall * 1e-3),
+                     "ms_per_step": ms_wall,
+                     "config": {"workload": "recurrent decode: 512 sequences x 1 token, H=32, K=V=128, bf16 q/k/v, "
+                                            "fp32 g/beta, states updated in place in a bf16 cache [4096,32,128,128] "
+                                            "with a 4096-element row gap", "global_batch": nseq, "seq_len": 1,
+                                "seed": args.seed},
+                     "roofline": {"bound": "hbm", "achieved": nbytes / (ms_ev * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
+                                  "unit": "GB/s", "frac": nbytes / (ms_ev * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                                  "traffic": None, "kernel": "recurrent_decode_kernel",
+                                  "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": ms_ev}})
+        return base
     if args.workload == "varlen":
         lengths = wl.lengths_varlen(args.seed)
         inp = wl.device_prefill_inputs(lengths, H, K, V, dtype="bf16", seed=args.seed, device=dev, init_dtype="f32")
@@ -303,11 +326,12 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true", help="run only a plain 1 GiB device copy")
-    ap.add_argument("--workload", default="e2e", choices=["e2e", "varlen", "long", "copy", "ckpt"],
+    ap.add_argument("--workload", default="e2e", choices=["e2e", "varlen", "long", "copy", "ckpt", "decode"],
                     help="e2e (default, the headline step); varlen / long: the chunk prefill on 16 sequences of "
                          "512-4096 tokens / one 65536-token sequence (state gathered from and scattered to a bf16 "
                          "cache for long); copy: state gather/scatter on an fp32 [1024,32,128,128] cache; ckpt: "
-                         "the e2e step plus checkpoints every 1024 tokens scattered into cache rows")
+                         "the e2e step plus checkpoints every 1024 tokens scattered into cache rows; decode: one recurrent "
+                         "decode step of 512 sequences against a bf16 [4096,32,128,128] cache")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

@@ -8,6 +8,8 @@
  *   2. kda_chunk_prefill  -- run the chunkwise gated delta rule (chunk size
  *                            64) over a varlen batch delimited by cu_seqlens;
  *   3. kda_state_scatter  -- copy the final states back into cache rows.
+ * Decode has one: kda_recurrent_decode advances each sequence by one token
+ * with its state updated in place in its cache row.
  *
  * Sources (web pages, cited by title and section):
  *  [P1] "vllm-ascend 的 KDA 状态复制 Triton 集成：PR 17301 对齐的预编译 worker
@@ -205,6 +207,56 @@ size_t kda_chunk_prefill_workspace_size(int64_t T, int64_t N, int64_t H, int64_t
  * KDA_E_UNSUPPORTED, KDA_E_WORKSPACE, KDA_E_ALIAS, KDA_E_HIP.
  */
 kda_status_t kda_chunk_prefill(const kda_prefill_args_t* args, void* stream);
+
+/*
+ * Arguments of kda_recurrent_decode: one new token for each of N sequences.
+ * All pointers are device pointers to contiguous row-major arrays.
+ *  N, H, K, V      -- sequences (= tokens), heads, key dim (1..128), value dim (>= 1);
+ *                     H, V, K must equal the cache's.
+ *  q, k            -- [N, H, K] in qkv_dtype.       v -- [N, H, V] in qkv_dtype.
+ *  g               -- [N, H, K] fp32 natural-log decays (state multiplied by exp(g)).
+ *  beta            -- [N, H] in beta_dtype.
+ *  state_indices   -- [N] int32 (KDA_I32) or int64 (KDA_I64): the cache row
+ *                     holding sequence n's state, read in its own width.
+ *  out             -- [N, H, V] in qkv_dtype; may be exactly v.
+ *  scale, use_qk_l2norm -- as for kda_chunk_prefill.
+ */
+typedef struct {
+  int64_t N, H, K, V;
+  const void* q;
+  const void* k;
+  const void* v;
+  kda_dtype_t qkv_dtype;
+  const float* g;
+  const void* beta;
+  kda_dtype_t beta_dtype;
+  const void* state_indices;
+  kda_index_t index_type;
+  void* out;
+  float scale;
+  int use_qk_l2norm;
+} kda_decode_args_t;
+
+/*
+ * kda_recurrent_decode -- one step of the gated delta rule per sequence with
+ * the state updated in place in its cache row ([P2] section 1.1 for one
+ * token; decode runs its own recurrent kernel on the indexed state rows, [P1]
+ * section "背景" and [P3] section "实现拆解").  For each n with
+ * r = state_indices[n] in [0, num_rows) and each head h, with S the K x V
+ * state of cache row r, head h (element (r,h,v,c) = S[c][v]):
+ *   S <- (I - beta k^ k^T) Diag(exp g) S + beta k^ v^T   (written back to row r,
+ *                                                       rounded to the cache dtype)
+ *   out[n,h,:] = scale * S^T q^
+ * computed in fp32.  An index outside [0, num_rows) marks a padding slot: its
+ * output is zero and no cache row is read or written.
+ * Preconditions (not checked, no device-to-host scan): valid indices are
+ * unique within one call (rows are updated concurrently).  out must not
+ * overlap the cache (checked against the cache's address span).
+ * N == 0 validates the cache view and enqueues nothing.
+ * Errors: KDA_E_NULL, KDA_E_DTYPE, KDA_E_SHAPE, KDA_E_LAYOUT, KDA_E_OVERLAP,
+ * KDA_E_UNSUPPORTED, KDA_E_ALIAS, KDA_E_HIP.
+ */
+kda_status_t kda_recurrent_decode(const kda_state_cache_t* cache, const kda_decode_args_t* args, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* kda_status_string(kda_status_t status);

@@ -14,7 +14,7 @@ STATUS_NAMES = {0: "KDA_OK", 1: "KDA_E_NULL", 2: "KDA_E_DTYPE", 3: "KDA_E_SHAPE"
                 5: "KDA_E_OVERLAP", 6: "KDA_E_UNSUPPORTED", 7: "KDA_E_WORKSPACE", 8: "KDA_E_ALIAS",
                 9: "KDA_E_HIP"}
 EXPORTED = ("kda_state_gather", "kda_state_scatter", "kda_chunk_prefill", "kda_chunk_prefill_workspace_size",
-            "kda_status_string", "kda_last_error_detail")
+            "kda_recurrent_decode", "kda_status_string", "kda_last_error_detail")
 
 
 class StateCache(ctypes.Structure):
@@ -36,6 +36,14 @@ class PrefillArgs(ctypes.Structure):
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("ckpt_interval", ctypes.c_int64), ("ckpt_cu", ctypes.c_void_p), ("ckpt_states", ctypes.c_void_p),
                 ("num_ckpt", ctypes.c_int64), ("ckpt_dtype", ctypes.c_int)]
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int64), ("H", ctypes.c_int64), ("K", ctypes.c_int64), ("V", ctypes.c_int64),
+                ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("qkv_dtype", ctypes.c_int),
+                ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("beta_dtype", ctypes.c_int),
+                ("state_indices", ctypes.c_void_p), ("index_type", ctypes.c_int),
+                ("out", ctypes.c_void_p), ("scale", ctypes.c_float), ("use_qk_l2norm", ctypes.c_int)]
 
 
 class KDAError(RuntimeError):
@@ -66,6 +74,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_state_scatter.restype = ctypes.c_int
     lib.kda_chunk_prefill.argtypes = [ctypes.POINTER(PrefillArgs), vp]
     lib.kda_chunk_prefill.restype = ctypes.c_int
+    lib.kda_recurrent_decode.argtypes = [ctypes.POINTER(StateCache), ctypes.POINTER(DecodeArgs), vp]
+    lib.kda_recurrent_decode.restype = ctypes.c_int
     lib.kda_chunk_prefill_workspace_size.argtypes = [i64, i64, i64, i64, i64]
     lib.kda_chunk_prefill_workspace_size.restype = ctypes.c_size_t
     lib.kda_status_string.argtypes = [ctypes.c_int]

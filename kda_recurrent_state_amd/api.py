@@ -13,7 +13,7 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import KDA_BF16, KDA_F32, KDA_I32, KDA_I64, KDAError, PrefillArgs, StateCache
+from ._lib import KDA_BF16, KDA_F32, KDA_I32, KDA_I64, DecodeArgs, KDAError, PrefillArgs, StateCache
 
 _DT = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
 
@@ -180,6 +180,55 @@ def kda_chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torc
     st = lib.kda_chunk_prefill(ctypes.byref(a), _stream_handle(stream))
     _lib.check("kda_chunk_prefill", st)
     return out, final_state
+
+
+def kda_recurrent_decode(cache: torch.Tensor, state_indices: torch.Tensor, q: torch.Tensor, k: torch.Tensor,
+                         v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor, out: Optional[torch.Tensor] = None,
+                         scale: Optional[float] = None, use_qk_l2norm: bool = True, stream=None) -> torch.Tensor:
+    """One decode token per sequence; cache rows state_indices[n] updated in place.
+
+    cache: [num_rows,H,V,K] view (fp32 or bf16, dense inner dims); state_indices:
+    [N] int32/int64 (outside [0,num_rows) = padding slot: zero output, no state
+    access); q, k, g: [N,H,K]; v: [N,H,V]; beta: [N,H].  Returns out [N,H,V]
+    (may be ``v``).  Valid indices must be unique.
+    """
+    lib = _lib.load_library()
+    _require_cuda(cache, state_indices, q, k, v, g, beta, out)
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
+        raise KDAError("kda_recurrent_decode", 3, "q,k must be [N,H,K] and v [N,H,V]")
+    N, H, K = (int(x) for x in q.shape)
+    V = int(v.shape[2])
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("state_indices", state_indices)):
+        if not t.is_contiguous():
+            raise KDAError("kda_recurrent_decode", 4, "%s must be contiguous" % name)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise KDAError("kda_recurrent_decode", 2, "q, k, v must share a dtype")
+    if g.dtype != torch.float32 or tuple(g.shape) != (N, H, K):
+        raise KDAError("kda_recurrent_decode", 2, "g must be float32 [N,H,K]")
+    if tuple(beta.shape) != (N, H):
+        raise KDAError("kda_recurrent_decode", 3, "beta must be [N,H]")
+    if state_indices.dim() != 1 or state_indices.numel() != N:
+        raise KDAError("kda_recurrent_decode", 3, "state_indices must be [N]")
+    if out is None:
+        out = torch.empty((N, H, V), dtype=q.dtype, device=q.device)
+    if out.dtype != q.dtype or tuple(out.shape) != (N, H, V) or not out.is_contiguous():
+        raise KDAError("kda_recurrent_decode", 3, "out must be a contiguous [N,H,V] tensor of q's dtype")
+    d = cache_descriptor(cache)
+    a = DecodeArgs()
+    a.N, a.H, a.K, a.V = N, H, K, V
+    a.q, a.k, a.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
+    a.qkv_dtype = _dtype_code(q, "kda_recurrent_decode")
+    a.g = g.data_ptr()
+    a.beta = beta.data_ptr()
+    a.beta_dtype = _dtype_code(beta, "kda_recurrent_decode")
+    a.state_indices = state_indices.data_ptr()
+    a.index_type = _index_code(state_indices)
+    a.out = out.data_ptr()
+    a.scale = float(K ** -0.5 if scale is None else scale)
+    a.use_qk_l2norm = 1 if use_qk_l2norm else 0
+    st = lib.kda_recurrent_decode(ctypes.byref(d), ctypes.byref(a), _stream_handle(stream))
+    _lib.check("kda_recurrent_decode", st)
+    return out
 
 
 def checkpoint_offsets(lengths, interval: int):

@@ -20,6 +20,9 @@ hipError_t launch_state_copy(bool gather, char* cache, int64_t row_stride_bytes,
 // Enqueues the chunked gated-delta-rule prefill; arguments already validated.
 hipError_t launch_chunk_prefill(const kda_prefill_args_t& a, hipStream_t stream);
 
+// Enqueues one recurrent decode step on validated arguments (cache and args agree).
+hipError_t launch_recurrent_decode(const kda_state_cache_t& cache, const kda_decode_args_t& a, hipStream_t stream);
+
 // Workspace bytes launch_chunk_prefill uses for these sizes.
 size_t chunk_prefill_workspace_bytes(int64_t T, int64_t N, int64_t H, int64_t K, int64_t V);
 

@@ -130,6 +130,33 @@ kda_status_t kda_chunk_prefill(const kda_prefill_args_t* a, void* stream) {
   return hip_status("kda_chunk_prefill launch", e);
 }
 
+kda_status_t kda_recurrent_decode(const kda_state_cache_t* cache, const kda_decode_args_t* a, void* stream) {
+  int64_t payload = 0;
+  kda_status_t st = check_cache(cache, &payload);
+  if (st != KDA_OK) return st;
+  if (!a) return KDA_E_NULL;
+  if (a->N < 0 || a->H <= 0 || a->K <= 0 || a->V <= 0) return KDA_E_SHAPE;
+  if (a->H != cache->H || a->V != cache->V || a->K != cache->K) return KDA_E_SHAPE;
+  if (!valid_dtype(a->qkv_dtype) || !valid_dtype(a->beta_dtype)) return KDA_E_DTYPE;
+  if (a->index_type != KDA_I32 && a->index_type != KDA_I64) return KDA_E_DTYPE;
+  if (a->K > 128) return KDA_E_UNSUPPORTED;
+  if (a->V * a->K * 4 >= ((int64_t)1 << 31)) return KDA_E_UNSUPPORTED;  // 32-bit offsets within a head's state
+  if (a->N > ((int64_t)1 << 40) / (a->H * (a->K > a->V ? a->K : a->V))) return KDA_E_SHAPE;
+  if (a->N == 0) return KDA_OK;
+  if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->state_indices || !a->out) return KDA_E_NULL;
+  const int64_t eb = dtype_bytes(a->qkv_dtype);
+  const int64_t ob = a->N * a->H * a->V * eb;
+  const int64_t kb = a->N * a->H * a->K * eb;
+  if (a->out != a->v && ranges_overlap(a->out, ob, a->v, ob)) return KDA_E_ALIAS;
+  if (ranges_overlap(a->out, ob, a->q, kb) || ranges_overlap(a->out, ob, a->k, kb) ||
+      ranges_overlap(a->out, ob, a->g, a->N * a->H * a->K * 4))
+    return KDA_E_ALIAS;
+  const int64_t span = ((cache->num_rows - 1) * cache->stride[0] + payload) * dtype_bytes(cache->dtype);
+  if (ranges_overlap(a->out, ob, cache->data, span)) return KDA_E_ALIAS;
+  hipError_t e = kda::launch_recurrent_decode(*cache, *a, static_cast<hipStream_t>(stream));
+  return hip_status("kda_recurrent_decode launch", e);
+}
+
 const char* kda_status_string(kda_status_t s) {
   switch (s) {
     case KDA_OK: return "KDA_OK";

@@ -17,6 +17,8 @@ What it provides (fp64, plain loops in ``kda_oracle.c``):
   "【轻量化复刻大模型 / KIMI K3】KDA 对 AI Infra 的挑战与各家应对", section 1.1).
 * :func:`checkpoint_states` -- states at every ``interval`` tokens of each
   sequence (prefix-boundary checkpoints), from the recurrence above.
+* :func:`recurrent_decode` -- one token per sequence against indexed state
+  rows (explicit-matrix form, numpy fp64); padding slots give zeros.
 * :mod:`oracle.chunk_form` -- the same map evaluated through the chunk
   decomposition stages of "PR #33465 完整报告" (section "关键源码片段"), in
   fp64 numpy; used to pin the chunk formulas, never by the product path.
@@ -203,6 +205,49 @@ def checkpoint_states(q, k, v, g, beta, cu_seqlens, interval, initial=None, scal
             cur[n] = fin[i]
             states[offs[n] + j] = fin[i]
     return states, offs
+
+
+def recurrent_decode(rows, indices, q, k, v, g, beta, scale=None, use_l2norm=True, eps=L2NORM_EPS):
+    """One decode token per sequence against indexed state rows, in fp64.
+
+    rows: [num_rows,H,V,K] states (element (r,h,v,c) = S[c][v]); indices: [N];
+    q, k, g: [N,H,K]; v: [N,H,V]; beta: [N,H].  For every n whose index r is in
+    [0, num_rows) and every head, the gated delta rule of "【轻量化复刻大模型 /
+    KIMI K3】KDA 对 AI Infra 的挑战与各家应对" (section 1.1) takes one step,
+        S <- (I - beta k^ k^T) Diag(exp g) S + beta k^ v^T,   o = scale S^T q^,
+    written here with explicit K x K matrices; other indices are padding slots
+    (zero output, no row touched).  Valid indices must be unique.
+    Returns (out [N,H,V] float64, new_rows [num_rows,H,V,K] float64).
+    """
+    new = np.array(rows, dtype=np.float64)
+    idx = [int(x) for x in np.asarray(indices).tolist()]
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    R, H, V, K = new.shape
+    N = len(idx)
+    if scale is None:
+        scale = K ** -0.5
+    valid = [r for r in idx if 0 <= r < R]
+    if len(set(valid)) != len(valid):
+        raise ValueError("valid state indices must be unique")
+    out = np.zeros((N, H, V), dtype=np.float64)
+    for n, r in enumerate(idx):
+        if not 0 <= r < R:
+            continue
+        for h in range(H):
+            kh, qh = k[n, h], q[n, h]
+            if use_l2norm:
+                kh = kh / np.sqrt(kh @ kh + eps)
+                qh = qh / np.sqrt(qh @ qh + eps)
+            S = new[r, h].T                                   # K x V
+            M = (np.eye(K) - beta[n, h] * np.outer(kh, kh)) @ np.diag(np.exp(g[n, h]))
+            S = M @ S + beta[n, h] * np.outer(kh, v[n, h])
+            out[n, h] = scale * S.T @ qh
+            new[r, h] = S.T
+    return out, new
 
 
 def default_threads() -> int:

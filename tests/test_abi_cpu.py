@@ -41,7 +41,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_python_binding_uses_the_c_names():
     import kda_recurrent_state_amd as k
-    for n in ("kda_state_gather", "kda_state_scatter", "kda_chunk_prefill", "kda_chunk_prefill_workspace_size"):
+    for n in ("kda_state_gather", "kda_state_scatter", "kda_chunk_prefill", "kda_chunk_prefill_workspace_size",
+              "kda_recurrent_decode"):
         assert callable(getattr(k, n))
 
 
@@ -136,6 +137,47 @@ def test_prefill_rejections(lib, kw, status):
 def test_prefill_empty_batch_is_ok(lib):
     a = _args(N=0, T=0)
     assert lib.kda_chunk_prefill(ctypes.byref(a), None) == 0
+
+
+def _dargs(**kw):
+    from kda_recurrent_state_amd._lib import DecodeArgs
+    a = DecodeArgs()
+    a.N, a.H, a.K, a.V = 3, 2, 4, 3
+    a.q, a.k, a.v, a.g, a.beta, a.out = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000, 0x600000
+    a.state_indices = 0x700000
+    a.qkv_dtype, a.beta_dtype, a.index_type = 1, 0, 0
+    a.scale = 0.5
+    a.use_qk_l2norm = 1
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("ckw,akw,status", [
+    ({}, dict(K=8), 3),                       # args disagree with the cache
+    ({}, dict(N=-1), 3),
+    ({}, dict(qkv_dtype=4), 2), ({}, dict(index_type=2), 2),
+    (dict(K=200), dict(K=200), 6),            # K > 128
+    ({}, dict(q=0), 1), ({}, dict(state_indices=0), 1), ({}, dict(out=0), 1),
+    ({}, dict(out=0x300000 + 2), 8),          # partial overlap with v
+    ({}, dict(out=0x200000), 8),              # overlaps k
+    ({}, dict(out=0x1000 + 8), 8),            # inside the cache span
+    (dict(strides=(24, 12, 3, 2)), {}, 4),    # inner dims not dense
+    (dict(strides=(10, 12, 4, 1)), {}, 5),    # rows overlap
+])
+def test_decode_rejections(lib, ckw, akw, status):
+    d = _cache(**ckw)
+    a = _dargs(**akw)
+    assert lib.kda_recurrent_decode(ctypes.byref(d), ctypes.byref(a), None) == status
+
+
+def test_decode_empty_batch_is_ok(lib):
+    d = _cache()
+    a = _dargs(N=0, q=0, k=0, v=0, g=0, beta=0, out=0, state_indices=0)
+    assert lib.kda_recurrent_decode(ctypes.byref(d), ctypes.byref(a), None) == 0
+    a = _dargs(out=0x300000)                  # out may be exactly v (no launch without a GPU: N=0)
+    a.N = 0
+    assert lib.kda_recurrent_decode(ctypes.byref(d), ctypes.byref(a), None) == 0
 
 
 def test_checkpoint_offsets_helper():
