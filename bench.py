@@ -187,6 +187,33 @@ def bench_other(args, dev):
                                   "kernel": "state_copy_kernel"},
                      "per_index_type": res})
         return base
+    if args.workload == "int8":
+        slots, S = 1024, 256
+        qd = torch.zeros((slots, H, V, K), dtype=torch.int8, device=dev)
+        sc = torch.zeros((slots, H, 1, K), dtype=torch.float32, device=dev)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(args.seed)
+        xs = torch.randn((S, H, V, K), generator=gen, device=dev) * 0.1
+        back = torch.empty_like(xs)
+        idx = torch.from_numpy(wl.rng(args.seed + 2).permutation(slots)[:S].astype(np.int32)).to(dev)
+        _, q_ms = _timed(lambda: kda.kda_ckpt_quantize_scatter(qd, sc, idx, xs), args.steps, args.warmup)
+        _, d_ms = _timed(lambda: kda.kda_ckpt_dequantize_gather(qd, sc, idx, packed=back), args.steps, args.warmup)
+        n = S * H * V * K
+        q_bytes = n * 4 + n + S * H * K * 4 + 4 * S
+        d_bytes = n + S * H * K * 4 + n * 4 + 4 * S
+        q_gbps, d_gbps = q_bytes / (q_ms * 1e-3) / 1e9, d_bytes / (d_ms * 1e-3) / 1e9
+        avg = (q_gbps + d_gbps) / 2
+        base.update({"metric": "INT8 checkpoint store/load GB/s, 1 GPU", "unit": "GB/s", "value": avg, "dtype": "f32",
+                     "ms_per_step": q_ms + d_ms,
+                     "config": {"workload": "INT8 checkpoint codec: 256 fp32 states [32,128,128] quantised into "
+                                            "a 1024-slot int8 store and dequantised back to fp32", "seq_len": None,
+                                "seed": args.seed},
+                     "roofline": {"bound": "hbm", "achieved": avg, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                  "frac": avg / HBM_PEAK_GBPS, "traffic": None,
+                                  "kernel": "quantize_scatter_kernel + dequantize_gather_kernel"},
+                     "per_kernel": {"quantize_GBps": q_gbps, "quantize_ms": q_ms, "quantize_bytes": q_bytes,
+                                    "dequantize_GBps": d_gbps, "dequantize_ms": d_ms, "dequantize_bytes": d_bytes}})
+        return base
     if args.workload == "decode":
         nseq, nrows = 512, NUM_ROWS
         back, off, shape, strides = wl.device_cache(nrows, H, V, K, dtype="bf16", gap=wl.GAP, offset=0,
@@ -326,12 +353,13 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true", help="run only a plain 1 GiB device copy")
-    ap.add_argument("--workload", default="e2e", choices=["e2e", "varlen", "long", "copy", "ckpt", "decode"],
+    ap.add_argument("--workload", default="e2e", choices=["e2e", "varlen", "long", "copy", "ckpt", "decode", "int8"],
                     help="e2e (default, the headline step); varlen / long: the chunk prefill on 16 sequences of "
                          "512-4096 tokens / one 65536-token sequence (state gathered from and scattered to a bf16 "
                          "cache for long); copy: state gather/scatter on an fp32 [1024,32,128,128] cache; ckpt: "
                          "the e2e step plus checkpoints every 1024 tokens scattered into cache rows; decode: one recurrent "
-                         "decode step of 512 sequences against a bf16 [4096,32,128,128] cache")
+                         "decode step of 512 sequences against a bf16 [4096,32,128,128] cache; int8: the INT8 checkpoint "
+                         "codec on 256 fp32 states")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

@@ -9,7 +9,9 @@
  *                            64) over a varlen batch delimited by cu_seqlens;
  *   3. kda_state_scatter  -- copy the final states back into cache rows.
  * Decode has one: kda_recurrent_decode advances each sequence by one token
- * with its state updated in place in its cache row.
+ * with its state updated in place in its cache row.  Checkpoints can be
+ * parked compressed: kda_ckpt_quantize_scatter / kda_ckpt_dequantize_gather
+ * move states between packed buffers and an INT8 checkpoint store.
  *
  * Sources (web pages, cited by title and section):
  *  [P1] "vllm-ascend 的 KDA 状态复制 Triton 集成：PR 17301 对齐的预编译 worker
@@ -257,6 +259,54 @@ typedef struct {
  * KDA_E_UNSUPPORTED, KDA_E_ALIAS, KDA_E_HIP.
  */
 kda_status_t kda_recurrent_decode(const kda_state_cache_t* cache, const kda_decode_args_t* args, void* stream);
+
+/*
+ * A compressed (INT8) checkpoint store for one layer ([P2] section 5.3: parked
+ * checkpoints compressed to INT8 and dequantised into a fresh active slot on
+ * a hit; section 6.6.2: qdata [slots, heads, d_v, d_k] int8 and scale
+ * [slots, heads, 1, d_k]).
+ *  qdata         -- int8 codes; element (s, h, v, c) at qdata[s*qdata_stride0 + (h*V + v)*K + c].
+ *  scale         -- fp32 scales; element (s, h, c) at scale[s*scale_stride0 + h*K + c].
+ *  num_slots, H, V, K -- num_slots > 0, 1 <= K <= 128, H, V > 0.
+ *  qdata_stride0 >= H*V*K and scale_stride0 >= H*K (slots never overlap); the
+ *  qdata and scale address ranges must be disjoint.
+ */
+typedef struct {
+  int8_t* qdata;
+  float* scale;
+  int64_t num_slots, H, V, K;
+  int64_t qdata_stride0, scale_stride0;
+} kda_int8_store_t;
+
+/*
+ * kda_ckpt_quantize_scatter -- for i in [0, num_selected): if
+ * 0 <= indices[i] < num_slots, slot indices[i] receives packed[i] quantised
+ * per (head, key channel c):
+ *   amax_c  = max over v of |x[v][c]|,   scale_c = amax_c / 127   (fp32 division)
+ *   code    = clamp(rint(x[v][c] / scale_c), -127, 127)            (fp32 division,
+ *             ties to even), code = 0 where scale_c == 0.
+ * Other entries are skipped.  packed: [num_selected, H, V, K] in packed_dtype
+ * (fp32 or bf16), contiguous.  Preconditions (not checked): valid slots are
+ * unique; finite inputs.  num_selected == 0 enqueues nothing.
+ * Errors: KDA_E_NULL, KDA_E_DTYPE, KDA_E_SHAPE, KDA_E_OVERLAP, KDA_E_UNSUPPORTED,
+ * KDA_E_HIP.
+ */
+kda_status_t kda_ckpt_quantize_scatter(const kda_int8_store_t* store, const void* indices, kda_index_t index_type,
+                                       int64_t num_selected, const void* packed, kda_dtype_t packed_dtype,
+                                       void* stream);
+
+/*
+ * kda_ckpt_dequantize_gather -- for i in [0, num_selected):
+ *   packed[i][h][v][c] = code * scale_c (fp32, then rounded to packed_dtype)
+ *       if 0 <= indices[i] < num_slots and (flags == NULL or flags[i] != 0),
+ *   packed[i] = zeros otherwise.
+ * Every row of packed is written; the result can seed kda_chunk_prefill's
+ * initial_state or go to active cache rows through kda_state_scatter.
+ * Errors as for kda_ckpt_quantize_scatter.
+ */
+kda_status_t kda_ckpt_dequantize_gather(const kda_int8_store_t* store, const void* indices, kda_index_t index_type,
+                                        int64_t num_selected, const uint8_t* flags, void* packed,
+                                        kda_dtype_t packed_dtype, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* kda_status_string(kda_status_t status);

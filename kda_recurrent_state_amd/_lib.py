@@ -14,7 +14,8 @@ STATUS_NAMES = {0: "KDA_OK", 1: "KDA_E_NULL", 2: "KDA_E_DTYPE", 3: "KDA_E_SHAPE"
                 5: "KDA_E_OVERLAP", 6: "KDA_E_UNSUPPORTED", 7: "KDA_E_WORKSPACE", 8: "KDA_E_ALIAS",
                 9: "KDA_E_HIP"}
 EXPORTED = ("kda_state_gather", "kda_state_scatter", "kda_chunk_prefill", "kda_chunk_prefill_workspace_size",
-            "kda_recurrent_decode", "kda_status_string", "kda_last_error_detail")
+            "kda_recurrent_decode", "kda_ckpt_quantize_scatter", "kda_ckpt_dequantize_gather",
+            "kda_status_string", "kda_last_error_detail")
 
 
 class StateCache(ctypes.Structure):
@@ -44,6 +45,12 @@ class DecodeArgs(ctypes.Structure):
                 ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("beta_dtype", ctypes.c_int),
                 ("state_indices", ctypes.c_void_p), ("index_type", ctypes.c_int),
                 ("out", ctypes.c_void_p), ("scale", ctypes.c_float), ("use_qk_l2norm", ctypes.c_int)]
+
+
+class Int8Store(ctypes.Structure):
+    _fields_ = [("qdata", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("num_slots", ctypes.c_int64),
+                ("H", ctypes.c_int64), ("V", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("qdata_stride0", ctypes.c_int64), ("scale_stride0", ctypes.c_int64)]
 
 
 class KDAError(RuntimeError):
@@ -76,6 +83,11 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_prefill.restype = ctypes.c_int
     lib.kda_recurrent_decode.argtypes = [ctypes.POINTER(StateCache), ctypes.POINTER(DecodeArgs), vp]
     lib.kda_recurrent_decode.restype = ctypes.c_int
+    lib.kda_ckpt_quantize_scatter.argtypes = [ctypes.POINTER(Int8Store), vp, ctypes.c_int, i64, vp, ctypes.c_int, vp]
+    lib.kda_ckpt_quantize_scatter.restype = ctypes.c_int
+    lib.kda_ckpt_dequantize_gather.argtypes = [ctypes.POINTER(Int8Store), vp, ctypes.c_int, i64, vp, vp, ctypes.c_int,
+                                               vp]
+    lib.kda_ckpt_dequantize_gather.restype = ctypes.c_int
     lib.kda_chunk_prefill_workspace_size.argtypes = [i64, i64, i64, i64, i64]
     lib.kda_chunk_prefill_workspace_size.restype = ctypes.c_size_t
     lib.kda_status_string.argtypes = [ctypes.c_int]

@@ -13,7 +13,7 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import KDA_BF16, KDA_F32, KDA_I32, KDA_I64, DecodeArgs, KDAError, PrefillArgs, StateCache
+from ._lib import KDA_BF16, KDA_F32, KDA_I32, KDA_I64, DecodeArgs, Int8Store, KDAError, PrefillArgs, StateCache
 
 _DT = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
 
@@ -229,6 +229,67 @@ def kda_recurrent_decode(cache: torch.Tensor, state_indices: torch.Tensor, q: to
     st = lib.kda_recurrent_decode(ctypes.byref(d), ctypes.byref(a), _stream_handle(stream))
     _lib.check("kda_recurrent_decode", st)
     return out
+
+
+def int8_store_descriptor(qdata: torch.Tensor, scale: torch.Tensor) -> Int8Store:
+    """Describe an INT8 checkpoint store: qdata [num_slots,H,V,K] int8 and scale
+    [num_slots,H,1,K] (or [num_slots,H,K]) fp32, inner dims dense, any slot stride."""
+    if qdata.dim() != 4 or qdata.dtype != torch.int8:
+        raise KDAError("int8 store", 2, "qdata must be an int8 [num_slots,H,V,K] tensor")
+    S, H, V, K = (int(x) for x in qdata.shape)
+    if scale.dtype != torch.float32 or scale.shape[0] != S or scale.numel() != S * H * K:
+        raise KDAError("int8 store", 2, "scale must be float32 [num_slots,H,1,K]")
+    sc = scale.reshape(S, H, K) if scale.dim() == 4 else scale
+    if tuple(qdata.stride()[1:]) != (V * K, K, 1) or tuple(sc.stride()[1:]) != (K, 1):
+        raise KDAError("int8 store", 4, "qdata [H,V,K] and scale [H,K] must be dense within a slot")
+    d = Int8Store()
+    d.qdata, d.scale = qdata.data_ptr(), scale.data_ptr()
+    d.num_slots, d.H, d.V, d.K = S, H, V, K
+    d.qdata_stride0, d.scale_stride0 = int(qdata.stride(0)), int(sc.stride(0))
+    return d
+
+
+def kda_ckpt_quantize_scatter(qdata: torch.Tensor, scale: torch.Tensor, indices: torch.Tensor, packed: torch.Tensor,
+                              stream=None) -> None:
+    """Slots indices[i] of the INT8 store <- quantised packed[i] (invalid slots skipped)."""
+    lib = _lib.load_library()
+    _require_cuda(qdata, scale, indices, packed)
+    if indices.dim() != 1 or not indices.is_contiguous():
+        raise KDAError("kda_ckpt_quantize_scatter", 3, "indices must be a contiguous 1-D tensor")
+    S = int(indices.shape[0])
+    if tuple(packed.shape) != (S,) + tuple(qdata.shape[1:]) or not packed.is_contiguous():
+        raise KDAError("kda_ckpt_quantize_scatter", 3, "packed must be a contiguous [S,H,V,K] tensor")
+    d = int8_store_descriptor(qdata, scale)
+    st = lib.kda_ckpt_quantize_scatter(ctypes.byref(d), indices.data_ptr(), _index_code(indices), S,
+                                       packed.data_ptr(), _dtype_code(packed, "kda_ckpt_quantize_scatter"),
+                                       _stream_handle(stream))
+    _lib.check("kda_ckpt_quantize_scatter", st)
+
+
+def kda_ckpt_dequantize_gather(qdata: torch.Tensor, scale: torch.Tensor, indices: torch.Tensor,
+                               flags: Optional[torch.Tensor] = None, packed: Optional[torch.Tensor] = None,
+                               dtype: torch.dtype = torch.float32, stream=None) -> torch.Tensor:
+    """packed[i] = dequantised slot indices[i] if valid and flagged, else zeros."""
+    lib = _lib.load_library()
+    _require_cuda(qdata, scale, indices, flags, packed)
+    if indices.dim() != 1 or not indices.is_contiguous():
+        raise KDAError("kda_ckpt_dequantize_gather", 3, "indices must be a contiguous 1-D tensor")
+    S = int(indices.shape[0])
+    if packed is None:
+        packed = torch.empty((S,) + tuple(qdata.shape[1:]), dtype=dtype, device=qdata.device)
+    if tuple(packed.shape) != (S,) + tuple(qdata.shape[1:]) or not packed.is_contiguous():
+        raise KDAError("kda_ckpt_dequantize_gather", 3, "packed must be a contiguous [S,H,V,K] tensor")
+    fptr = None
+    if flags is not None:
+        if flags.dtype not in (torch.bool, torch.uint8) or flags.numel() != S or not flags.is_contiguous():
+            raise KDAError("kda_ckpt_dequantize_gather", 2, "flags must be a contiguous bool/uint8 tensor of length S")
+        fptr = flags.data_ptr()
+    d = int8_store_descriptor(qdata, scale)
+    st = lib.kda_ckpt_dequantize_gather(ctypes.byref(d), indices.data_ptr(), _index_code(indices), S, fptr,
+                                        packed.data_ptr(), _dtype_code(packed, "kda_ckpt_dequantize_gather"),
+                                        _stream_handle(stream))
+    _lib.check("kda_ckpt_dequantize_gather", st)
+    return packed
 
 
 def checkpoint_offsets(lengths, interval: int):

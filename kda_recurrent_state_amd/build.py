@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libkda.so")
-SOURCES = ["kda_api.cpp", "state_copy.hip", "chunk_prefill.hip", "decode.hip"]
+SOURCES = ["kda_api.cpp", "state_copy.hip", "chunk_prefill.hip", "decode.hip", "int8_ckpt.hip"]
 ARCH = "gfx950"
 
 

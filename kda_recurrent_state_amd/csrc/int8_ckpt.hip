@@ -1,0 +1,290 @@
+// INT8 checkpoint codec fused into the state copies.
+//
+// A compressed checkpoint store keeps, per slot and head, the K x V state as
+// int8 codes [V][K] plus one fp32 scale per key channel ([1][K]): the scale is
+// the largest magnitude over the d_v axis divided by 127 and the codes are
+// symmetric (page "【轻量化复刻大模型 / KIMI K3】KDA 对 AI Infra 的挑战与各家应对",
+// section 5.3: parked checkpoints are compressed to INT8 and dequantised into
+// a fresh active slot on a hit; section 6.6.2: qdata [slots, heads, d_v, d_k]
+// int8, scale [slots, heads, 1, d_k], max-abs along d_v, symmetric codes).
+//
+//   quantize-scatter: store slot indices[i] <- Q(packed[i])   (invalid slots skipped)
+//   dequantize-gather: packed[i] <- D(store slot indices[i])  (zeros for invalid
+//                                                              slots or false flags)
+// Q: amax_c = max_v |x[v][c]|, scale_c = amax_c / 127 (fp32 division),
+//    code = clamp(rint(x / scale_c), -127, 127) (fp32 division, ties to even),
+//    code = 0 where scale_c = 0.
+// D: x = code * scale_c in fp32, then rounded to the packed dtype.
+//
+// One workgroup per (selected state, head).  Quantize: 16 lanes per row, each
+// holding 8 consecutive channels; 16 row groups; the rows stay in registers
+// (up to 128) between the column-max pass and the encode pass, so the source
+// is read once.  Dequantize: 16 lanes per row, 8 channels per lane, the code
+// loads of 8 rows issued before their conversion and stores.
+#include "internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int kQThreads = 256;
+constexpr int kQC = 8;                        // channels per lane, quantize
+constexpr int kQLanes = 16;                   // lanes per row, quantize (kQC * kQLanes = 128 channels)
+constexpr int kQGroups = kQThreads / kQLanes; // row groups, quantize
+constexpr int kQRows = 8;                     // rows per thread kept in registers (V <= 128)
+constexpr int kDLanes = 16;                   // lanes per row, dequantize
+constexpr int kDGroups = kQThreads / kDLanes; // row groups, dequantize
+
+struct Int8Params {
+  int8_t* q;          // element (0,0,0,0) of qdata
+  float* s;           // element (0,0,0,0) of scale
+  int64_t qs0, ss0;   // slot strides, elements
+  int64_t num_slots;
+  const void* idx;
+  int idx64;
+  const uint8_t* flags;
+  void* packed;       // [S, H, V, K]
+  int pbf16;
+  int64_t H, V, K;
+  int vec;            // K % 8 == 0 and every row slice aligned: vector I/O
+};
+
+__device__ __forceinline__ int64_t slot_of(const Int8Params& p, int64_t i) {
+  return p.idx64 ? static_cast<const int64_t*>(p.idx)[i] : (int64_t) static_cast<const int32_t*>(p.idx)[i];
+}
+
+__device__ __forceinline__ float ld_packed(const void* base, int64_t e, int bf) {
+  return bf ? __uint_as_float((unsigned)static_cast<const unsigned short*>(base)[e] << 16)
+            : static_cast<const float*>(base)[e];
+}
+
+__device__ __forceinline__ int encode(float x, float sc) {
+  if (sc == 0.f) return 0;
+  float r = rintf(x / sc);
+  r = r > 127.f ? 127.f : (r < -127.f ? -127.f : r);
+  return (int)r;
+}
+
+// kKeep: V <= kQGroups * kQRows, rows held in registers; else the encode pass
+// reads the rows again.
+template <bool kKeep>
+__global__ __launch_bounds__(kQThreads) void quantize_scatter_kernel(Int8Params p) {
+  __shared__ float red[kQGroups][128];
+  __shared__ float scl[128];
+  const int64_t i = blockIdx.x / p.H;
+  const int64_t h = blockIdx.x - i * p.H;
+  const int64_t slot = slot_of(p, i);
+  if (slot < 0 || slot >= p.num_slots) return;
+  const int V = (int)p.V, K = (int)p.K;
+  const int tid = threadIdx.x;
+  const int lane = tid % kQLanes, grp = tid / kQLanes;
+  const int c0 = kQC * lane;  // this lane's first channel
+  const int64_t src = (i * p.H + h) * p.V * p.K;  // element offset of the source slice
+  int8_t* qd = p.q + slot * p.qs0 + h * p.V * p.K;
+  float* sd = p.s + slot * p.ss0 + h * p.K;
+
+  auto load = [&](int row, float (&x)[kQC]) {
+    const int64_t e = src + (int64_t)row * K + c0;
+    if (p.vec) {
+      if (p.pbf16) {
+        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const unsigned short*>(p.packed) + e);
+        const unsigned w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int t = 0; t < kQC; ++t)
+          x[t] = (t & 1) ? __uint_as_float(w[t >> 1] & 0xffff0000u) : __uint_as_float(w[t >> 1] << 16);
+      } else {
+        const float4 f0 = *reinterpret_cast<const float4*>(static_cast<const float*>(p.packed) + e);
+        const float4 f1 = *reinterpret_cast<const float4*>(static_cast<const float*>(p.packed) + e + 4);
+        x[0] = f0.x; x[1] = f0.y; x[2] = f0.z; x[3] = f0.w;
+        x[4] = f1.x; x[5] = f1.y; x[6] = f1.z; x[7] = f1.w;
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < kQC; ++t) x[t] = c0 + t < K ? ld_packed(p.packed, e + t, p.pbf16) : 0.f;
+    }
+  };
+
+  // pass 1: column max over this thread's rows
+  float keep[kKeep ? kQRows : 1][kQC];
+  float m[kQC];
+#pragma unroll
+  for (int t = 0; t < kQC; ++t) m[t] = 0.f;
+  if (c0 < K) {
+    if constexpr (kKeep) {
+#pragma unroll
+      for (int r = 0; r < kQRows; ++r) {
+        int row = grp + kQGroups * r;
+        row = row < V ? row : V - 1;  // clamped duplicates do not change the max
+        load(row, keep[r]);
+      }
+#pragma unroll
+      for (int r = 0; r < kQRows; ++r)
+#pragma unroll
+        for (int t = 0; t < kQC; ++t) m[t] = fmaxf(m[t], fabsf(keep[r][t]));
+    } else {
+      for (int row = grp; row < V; row += kQGroups) {
+        float x[kQC];
+        load(row, x);
+#pragma unroll
+        for (int t = 0; t < kQC; ++t) m[t] = fmaxf(m[t], fabsf(x[t]));
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kQC; ++t) red[grp][c0 + t] = m[t];
+  }
+  __syncthreads();
+  if (tid < K) {
+    float a = red[0][tid];
+#pragma unroll
+    for (int g = 1; g < kQGroups; ++g) a = fmaxf(a, red[g][tid]);
+    scl[tid] = a / 127.f;  // scale
+    sd[tid] = a / 127.f;
+  }
+  __syncthreads();
+  if (c0 >= K) return;
+  float sc[kQC];
+#pragma unroll
+  for (int t = 0; t < kQC; ++t) sc[t] = c0 + t < K ? scl[c0 + t] : 0.f;
+  auto store = [&](int row, const float (&x)[kQC]) {
+    int8_t* dst = qd + (int64_t)row * K + c0;
+    int qq[kQC];
+#pragma unroll
+    for (int t = 0; t < kQC; ++t) qq[t] = encode(x[t], sc[t]);
+    if (p.vec) {
+      unsigned w[2] = {0u, 0u};
+#pragma unroll
+      for (int t = 0; t < kQC; ++t) w[t >> 2] |= (unsigned)(qq[t] & 0xff) << (8 * (t & 3));
+      *reinterpret_cast<uint2*>(dst) = uint2{w[0], w[1]};
+    } else {
+#pragma unroll
+      for (int t = 0; t < kQC; ++t)
+        if (c0 + t < K) dst[t] = (int8_t)qq[t];
+    }
+  };
+  if constexpr (kKeep) {
+#pragma unroll
+    for (int r = 0; r < kQRows; ++r) {
+      const int row = grp + kQGroups * r;
+      if (row < V) store(row, keep[r]);
+    }
+  } else {
+    for (int row = grp; row < V; row += kQGroups) {
+      float x[kQC];
+      load(row, x);
+      store(row, x);
+    }
+  }
+}
+
+constexpr int kDRows = 8;  // rows per thread per batch, dequantize (loads issued together)
+
+__device__ __forceinline__ void store8(void* packed, int bf, int vec, int64_t e, int c0, int K, const float (&x)[8]) {
+  if (vec) {
+    if (bf) {
+      typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+      bf8 o;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) o[t] = (__bf16)x[t];
+      *reinterpret_cast<bf8*>(static_cast<__bf16*>(packed) + e) = o;
+    } else {
+      float* d = static_cast<float*>(packed) + e;
+      *reinterpret_cast<float4*>(d) = float4{x[0], x[1], x[2], x[3]};
+      *reinterpret_cast<float4*>(d + 4) = float4{x[4], x[5], x[6], x[7]};
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (c0 + t >= K) continue;
+      if (bf)
+        static_cast<__bf16*>(packed)[e + t] = (__bf16)x[t];
+      else
+        static_cast<float*>(packed)[e + t] = x[t];
+    }
+  }
+}
+
+__global__ __launch_bounds__(kQThreads) void dequantize_gather_kernel(Int8Params p) {
+  const int64_t i = blockIdx.x / p.H;
+  const int64_t h = blockIdx.x - i * p.H;
+  const int64_t slot = slot_of(p, i);
+  const bool take = slot >= 0 && slot < p.num_slots && (p.flags == nullptr || p.flags[i] != 0);
+  const int V = (int)p.V, K = (int)p.K;
+  const int tid = threadIdx.x;
+  const int lane = tid % kDLanes, grp = tid / kDLanes;
+  const int64_t dst = (i * p.H + h) * p.V * p.K;  // element offset of the packed slice
+  const int8_t* qs = take ? p.q + slot * p.qs0 + h * p.V * p.K : nullptr;
+  const float* ss = take ? p.s + slot * p.ss0 + h * p.K : nullptr;
+  for (int cb = 0; cb < K; cb += 8 * kDLanes) {
+    const int c0 = cb + 8 * lane;
+    if (c0 >= K) continue;
+    float sc[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) sc[t] = (take && c0 + t < K) ? ss[c0 + t] : 0.f;
+    for (int r0 = grp; r0 < V; r0 += kDGroups * kDRows) {
+      // every code load of the batch first
+      uint2 u[kDRows];
+      if (take && p.vec) {
+#pragma unroll
+        for (int r = 0; r < kDRows; ++r) {
+          int row = r0 + kDGroups * r;
+          row = row < V ? row : V - 1;
+          u[r] = *reinterpret_cast<const uint2*>(qs + (int64_t)row * K + c0);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < kDRows; ++r) {
+        const int row = r0 + kDGroups * r;
+        if (row >= V) break;
+        float x[8];
+        if (take && p.vec) {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const unsigned w = t < 4 ? u[r].x : u[r].y;
+            x[t] = (float)(int8_t)((w >> (8 * (t & 3))) & 0xff) * sc[t];
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            x[t] = (take && c0 + t < K) ? (float)qs[(int64_t)row * K + c0 + t] * sc[t] : 0.f;
+        }
+        store8(p.packed, p.pbf16, p.vec, dst + (int64_t)row * K + c0, c0, K, x);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_int8_ckpt(bool quantize, const kda_int8_store_t& st, const void* indices, bool index64,
+                            int64_t num_selected, const uint8_t* flags, void* packed, bool packed_bf16,
+                            hipStream_t stream) {
+  Int8Params p;
+  p.q = st.qdata;
+  p.s = st.scale;
+  p.qs0 = st.qdata_stride0;
+  p.ss0 = st.scale_stride0;
+  p.num_slots = st.num_slots;
+  p.idx = indices;
+  p.idx64 = index64;
+  p.flags = flags;
+  p.packed = packed;
+  p.pbf16 = packed_bf16;
+  p.H = st.H;
+  p.V = st.V;
+  p.K = st.K;
+  const int64_t eb = packed_bf16 ? 2 : 4;
+  // vector I/O: 8-channel groups whole, packed rows 16-byte aligned, int8 rows 8-byte aligned
+  p.vec = st.K % 8 == 0 && (uintptr_t)packed % 16 == 0 && (st.K * eb) % 16 == 0 && (uintptr_t)st.qdata % 8 == 0 &&
+          st.qdata_stride0 % 8 == 0;
+  const dim3 grid((unsigned)(num_selected * st.H)), block(kQThreads);
+  if (quantize) {
+    if (st.V <= kQGroups * kQRows)
+      hipLaunchKernelGGL(quantize_scatter_kernel<true>, grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL(quantize_scatter_kernel<false>, grid, block, 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(dequantize_gather_kernel, grid, block, 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kda

@@ -23,6 +23,12 @@ hipError_t launch_chunk_prefill(const kda_prefill_args_t& a, hipStream_t stream)
 // Enqueues one recurrent decode step on validated arguments (cache and args agree).
 hipError_t launch_recurrent_decode(const kda_state_cache_t& cache, const kda_decode_args_t& a, hipStream_t stream);
 
+// INT8 checkpoint codec: quantize-scatter (packed -> store slots) or
+// dequantize-gather (store slots -> packed); arguments already validated.
+hipError_t launch_int8_ckpt(bool quantize, const kda_int8_store_t& store, const void* indices, bool index64,
+                            int64_t num_selected, const uint8_t* flags, void* packed, bool packed_bf16,
+                            hipStream_t stream);
+
 // Workspace bytes launch_chunk_prefill uses for these sizes.
 size_t chunk_prefill_workspace_bytes(int64_t T, int64_t N, int64_t H, int64_t K, int64_t V);
 

@@ -77,6 +77,30 @@ bool ranges_overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes
   return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
 }
 
+kda_status_t int8_common(bool quantize, const kda_int8_store_t* st, const void* indices, kda_index_t it,
+                         int64_t num_selected, const uint8_t* flags, void* packed, kda_dtype_t pdt, void* stream) {
+  if (!st) return KDA_E_NULL;
+  if (st->num_slots <= 0 || st->H <= 0 || st->V <= 0 || st->K <= 0) return KDA_E_SHAPE;
+  if (st->K > 128) return KDA_E_UNSUPPORTED;
+  if (st->H * st->V > ((int64_t)1 << 40) / st->K) return KDA_E_SHAPE;
+  const int64_t qpay = st->H * st->V * st->K, spay = st->H * st->K;
+  if (st->qdata_stride0 < qpay || st->scale_stride0 < spay) return KDA_E_OVERLAP;
+  if (st->qdata_stride0 > ((int64_t)1 << 46) / st->num_slots || st->scale_stride0 > ((int64_t)1 << 46) / st->num_slots)
+    return KDA_E_SHAPE;
+  if (!st->qdata || !st->scale) return KDA_E_NULL;
+  if (ranges_overlap(st->qdata, (st->num_slots - 1) * st->qdata_stride0 + qpay, st->scale,
+                     ((st->num_slots - 1) * st->scale_stride0 + spay) * 4))
+    return KDA_E_OVERLAP;
+  if (!valid_dtype(pdt)) return KDA_E_DTYPE;
+  if (it != KDA_I32 && it != KDA_I64) return KDA_E_DTYPE;
+  if (num_selected < 0) return KDA_E_SHAPE;
+  if (num_selected == 0) return KDA_OK;
+  if (!indices || !packed) return KDA_E_NULL;
+  hipError_t e = kda::launch_int8_ckpt(quantize, *st, indices, it == KDA_I64, num_selected, quantize ? nullptr : flags,
+                                       packed, pdt == KDA_BF16, static_cast<hipStream_t>(stream));
+  return hip_status(quantize ? "kda_ckpt_quantize_scatter launch" : "kda_ckpt_dequantize_gather launch", e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -155,6 +179,19 @@ kda_status_t kda_recurrent_decode(const kda_state_cache_t* cache, const kda_deco
   if (ranges_overlap(a->out, ob, cache->data, span)) return KDA_E_ALIAS;
   hipError_t e = kda::launch_recurrent_decode(*cache, *a, static_cast<hipStream_t>(stream));
   return hip_status("kda_recurrent_decode launch", e);
+}
+
+kda_status_t kda_ckpt_quantize_scatter(const kda_int8_store_t* store, const void* indices, kda_index_t index_type,
+                                       int64_t num_selected, const void* packed, kda_dtype_t packed_dtype,
+                                       void* stream) {
+  return int8_common(true, store, indices, index_type, num_selected, nullptr, const_cast<void*>(packed),
+                     packed_dtype, stream);
+}
+
+kda_status_t kda_ckpt_dequantize_gather(const kda_int8_store_t* store, const void* indices, kda_index_t index_type,
+                                        int64_t num_selected, const uint8_t* flags, void* packed,
+                                        kda_dtype_t packed_dtype, void* stream) {
+  return int8_common(false, store, indices, index_type, num_selected, flags, packed, packed_dtype, stream);
 }
 
 const char* kda_status_string(kda_status_t s) {

@@ -19,6 +19,9 @@ What it provides (fp64, plain loops in ``kda_oracle.c``):
   sequence (prefix-boundary checkpoints), from the recurrence above.
 * :func:`recurrent_decode` -- one token per sequence against indexed state
   rows (explicit-matrix form, numpy fp64); padding slots give zeros.
+* :func:`int8_quantize` / :func:`int8_dequantize` and the store/load
+  contracts :func:`int8_quantize_scatter` / :func:`int8_dequantize_gather`
+  -- the INT8 checkpoint codec (numpy, decisions in fp32).
 * :mod:`oracle.chunk_form` -- the same map evaluated through the chunk
   decomposition stages of "PR #33465 完整报告" (section "关键源码片段"), in
   fp64 numpy; used to pin the chunk formulas, never by the product path.
@@ -248,6 +251,62 @@ def recurrent_decode(rows, indices, q, k, v, g, beta, scale=None, use_l2norm=Tru
             out[n, h] = scale * S.T @ qh
             new[r, h] = S.T
     return out, new
+
+
+def int8_quantize(states):
+    """Symmetric INT8 codes of states [S,H,V,K] with one scale per (slot, head,
+    key channel): scale = (max over V of |x|) / 127, code = round-half-even of
+    x / scale clamped to [-127, 127], code 0 where the scale is 0 (page
+    "【轻量化复刻大模型 / KIMI K3】KDA 对 AI Infra 的挑战与各家应对", sections
+    5.3 and 6.6.2: max-abs along d_v, symmetric).  The decisions are taken in
+    fp32, the precision of the stored scale.  Returns (codes int8 [S,H,V,K],
+    scales float32 [S,H,1,K])."""
+    x = np.asarray(states, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=2, keepdims=True)
+    scale = (amax / np.float32(127.0)).astype(np.float32)
+    safe = np.where(scale == 0, np.float32(1.0), scale)
+    codes = np.clip(np.rint(x / safe), -127, 127)
+    codes = np.where(scale == 0, 0, codes).astype(np.int8)
+    return codes, scale
+
+
+def int8_dequantize(codes, scales):
+    """code * scale in fp32 ([S,H,V,K] float32)."""
+    return (np.asarray(codes, dtype=np.int8).astype(np.float32) * np.asarray(scales, dtype=np.float32)).astype(
+        np.float32)
+
+
+def int8_quantize_scatter(qdata, scale, indices, packed):
+    """Store side of the codec: slot indices[i] <- int8_quantize(packed[i]) for
+    indices in [0, num_slots); others skipped (the copy contract of page
+    "vllm-ascend 的 KDA 状态复制 Triton 集成", section "数值契约", applied to the
+    compressed store).  qdata [num_slots,H,V,K] int8 and scale
+    [num_slots,H,1,K] float32 are updated copies; returns (qdata, scale)."""
+    qd = np.array(qdata, dtype=np.int8)
+    sc = np.array(scale, dtype=np.float32)
+    codes, scales = int8_quantize(packed)
+    idx = [int(x) for x in np.asarray(indices).tolist()]
+    valid = [r for r in idx if 0 <= r < qd.shape[0]]
+    if len(set(valid)) != len(valid):
+        raise ValueError("valid slot indices must be unique")
+    for i, r in enumerate(idx):
+        if 0 <= r < qd.shape[0]:
+            qd[r] = codes[i]
+            sc[r] = scales[i]
+    return qd, sc
+
+
+def int8_dequantize_gather(qdata, scale, indices, flags=None):
+    """Load side: packed[i] = int8_dequantize(slot indices[i]) when the index is
+    in [0, num_slots) and flags[i] (if given) is nonzero, else zeros.
+    Returns float32 [S,H,V,K]."""
+    qd = np.asarray(qdata, dtype=np.int8)
+    idx = [int(x) for x in np.asarray(indices).tolist()]
+    out = np.zeros((len(idx),) + qd.shape[1:], dtype=np.float32)
+    for i, r in enumerate(idx):
+        if 0 <= r < qd.shape[0] and (flags is None or int(flags[i]) != 0):
+            out[i] = int8_dequantize(qd[r], np.asarray(scale)[r])
+    return out
 
 
 def default_threads() -> int:

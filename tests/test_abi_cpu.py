@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
 def test_python_binding_uses_the_c_names():
     import kda_recurrent_state_amd as k
     for n in ("kda_state_gather", "kda_state_scatter", "kda_chunk_prefill", "kda_chunk_prefill_workspace_size",
-              "kda_recurrent_decode"):
+              "kda_recurrent_decode", "kda_ckpt_quantize_scatter", "kda_ckpt_dequantize_gather"):
         assert callable(getattr(k, n))
 
 
@@ -178,6 +178,42 @@ def test_decode_empty_batch_is_ok(lib):
     a = _dargs(out=0x300000)                  # out may be exactly v (no launch without a GPU: N=0)
     a.N = 0
     assert lib.kda_recurrent_decode(ctypes.byref(d), ctypes.byref(a), None) == 0
+
+
+def _store(**kw):
+    from kda_recurrent_state_amd._lib import Int8Store
+    d = Int8Store()
+    d.qdata, d.scale = 0x100000, 0x900000
+    d.num_slots, d.H, d.V, d.K = 4, 2, 3, 8
+    d.qdata_stride0, d.scale_stride0 = 2 * 3 * 8 + 8, 2 * 8
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_slots=0), 3), (dict(K=0), 3), (dict(V=-1), 3),
+    (dict(K=130, qdata_stride0=2 * 3 * 130, scale_stride0=260), 6),
+    (dict(qdata_stride0=47), 5), (dict(scale_stride0=15), 5),
+    (dict(qdata=0), 1), (dict(scale=0), 1),
+    (dict(scale=0x100000 + 100), 5),             # scale inside the qdata range
+])
+def test_int8_store_rejections(lib, kw, status):
+    d = _store(**kw)
+    assert lib.kda_ckpt_quantize_scatter(ctypes.byref(d), 0x1000, 0, 2, 0x2000, 0, None) == status
+    assert lib.kda_ckpt_dequantize_gather(ctypes.byref(d), 0x1000, 0, 2, None, 0x2000, 0, None) == status
+
+
+def test_int8_selection_arguments(lib):
+    d = _store()
+    assert lib.kda_ckpt_quantize_scatter(ctypes.byref(d), 0x1000, 2, 2, 0x2000, 0, None) == 2     # index type
+    assert lib.kda_ckpt_quantize_scatter(ctypes.byref(d), 0x1000, 0, 2, 0x2000, 7, None) == 2     # packed dtype
+    assert lib.kda_ckpt_quantize_scatter(ctypes.byref(d), 0x1000, 0, -1, 0x2000, 0, None) == 3
+    assert lib.kda_ckpt_quantize_scatter(ctypes.byref(d), None, 0, 2, 0x2000, 0, None) == 1
+    assert lib.kda_ckpt_dequantize_gather(ctypes.byref(d), 0x1000, 0, 2, None, None, 1, None) == 1
+    # an empty selection validates and enqueues nothing
+    assert lib.kda_ckpt_quantize_scatter(ctypes.byref(d), None, 0, 0, None, 1, None) == 0
+    assert lib.kda_ckpt_dequantize_gather(ctypes.byref(d), None, 1, 0, None, None, 0, None) == 0
 
 
 def test_checkpoint_offsets_helper():
