@@ -65,6 +65,22 @@ def stored_traffic(T: int, N: int):
     return int(rec["hbm_bytes_per_launch"])
 
 
+def stored_kernel_traffic(json_name: str, kernel_prefix: str):
+    """HBM bytes per launch (read + write) of one kernel from a committed
+    rocprofv3 counter summary, if it was taken on the current source."""
+    path = os.path.join(ROOT, "profiles", json_name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != sha256_file(os.path.join(ROOT, rec["source"])):
+        return None
+    hits = [v for k, v in rec["kernels"].items() if k.startswith(kernel_prefix)]
+    if len(hits) != 1:
+        return None
+    return int(hits[0]["hbm_read_bytes_per_launch"] + hits[0]["hbm_write_bytes_per_launch"])
+
+
 def build_workload(seed: int, device):
     import torch
     import kda_workloads as wl
@@ -212,7 +228,11 @@ def bench_other(args, dev):
                                   "frac": avg / HBM_PEAK_GBPS, "traffic": None,
                                   "kernel": "quantize_scatter_kernel + dequantize_gather_kernel"},
                      "per_kernel": {"quantize_GBps": q_gbps, "quantize_ms": q_ms, "quantize_bytes": q_bytes,
-                                    "dequantize_GBps": d_gbps, "dequantize_ms": d_ms, "dequantize_bytes": d_bytes}})
+                                    "quantize_traffic": stored_kernel_traffic("int8_codec_traffic.json",
+                                                                              "quantize_scatter_kernel"),
+                                    "dequantize_GBps": d_gbps, "dequantize_ms": d_ms, "dequantize_bytes": d_bytes,
+                                    "dequantize_traffic": stored_kernel_traffic("int8_codec_traffic.json",
+                                                                                "dequantize_gather_kernel")}})
         return base
     if args.workload == "decode":
         nseq, nrows = 512, NUM_ROWS
@@ -234,7 +254,8 @@ def bench_other(args, dev):
                                 "seed": args.seed},
                      "roofline": {"bound": "hbm", "achieved": nbytes / (ms_ev * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
                                   "unit": "GB/s", "frac": nbytes / (ms_ev * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                                  "traffic": None, "kernel": "recurrent_decode_kernel",
+                                  "traffic": stored_kernel_traffic("decode_traffic.json", "recurrent_decode_kernel"),
+                                  "kernel": "recurrent_decode_kernel",
                                   "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": ms_ev}})
         return base
     if args.workload == "varlen":
