@@ -1000,73 +1000,77 @@ __global__ __launch_bounds__(1024) void seg_plan_kernel(const int32_t* __restric
   }
 }
 
-// Composes the segment maps of one (sequence, head) in fp32 (one workgroup of
-// 256 threads; K, V <= 128).  Writes each segment's initial state S_in
-// ([nmax, H, V, K] fp32) and the sequence's final state.
+// Composes the segment maps of one (sequence, head) in fp32, for one block
+// of kScanCols value columns (the columns of S evolve independently under
+// S <- M S + b); 256 threads, K, V <= 128.  Writes each segment's initial
+// state S_in ([nmax, H, V, K] fp32) and the sequence's final state for these
+// columns.
+constexpr int kScanCols = 16;
+
 __global__ __launch_bounds__(256) void seg_scan_kernel(const int32_t* __restrict__ sfirst, const float* __restrict__ bmap,
                                                        const float* __restrict__ mmap, const void* __restrict__ init,
                                                        int init_bf16, void* __restrict__ fin, int fin_bf16,
                                                        float* __restrict__ sin, int64_t H, int64_t K, int64_t V) {
-  __shared__ float sS[128 * 129];  // S[c][v]
-  __shared__ float sM[128 * 129];  // M[c][c']
-  const int64_t n = blockIdx.x / H, h = blockIdx.x % H;
+  __shared__ float sS[128][kScanCols + 1];  // S[c][v - v0]
+  __shared__ float sM[128][129];            // M[c][c']
+  const int64_t ncb = (V + kScanCols - 1) / kScanCols;
+  const int64_t item = blockIdx.x / ncb;
+  const int64_t v0 = (blockIdx.x - item * ncb) * kScanCols;
+  const int64_t n = item / H, h = item % H;
   const int tid = threadIdx.x;
   const int64_t srow = (n * H + h) * V;  // [.., H, V, K] row base of (n, h)
-  for (int e = tid; e < 128 * 128; e += 256) {
-    const int c = e & 127, v = e >> 7;
+  // coalesced element order: e -> (column vl, channel c), c fastest
+  for (int e = tid; e < kScanCols * 128; e += 256) {
+    const int c = e & 127, vl = e >> 7;
     float x = 0.f;
-    if (init && c < K && v < V) {
-      const int64_t o = (srow + v) * K + c;
+    if (init && c < K && v0 + vl < V) {
+      const int64_t o = (srow + v0 + vl) * K + c;
       x = init_bf16 ? bf2f(static_cast<const unsigned short*>(init)[o]) : static_cast<const float*>(init)[o];
     }
-    sS[c * 129 + v] = x;
+    sS[c][vl] = x;
   }
   __syncthreads();
-  const int r0 = 8 * (tid >> 4), c0 = 8 * (tid & 15);  // this thread's 8x8 block of S[c][v]
+  const int r = tid >> 1;                 // this thread's state row (key channel)
+  const int j0 = (tid & 1) * (kScanCols / 2);  // and its 8 columns
   for (int64_t sg = sfirst[n]; sg < sfirst[n + 1]; ++sg) {
     const int64_t srow_s = (sg * H + h) * V;
     const int64_t mrow_s = (sg * H + h) * K;
+    for (int e = tid; e < kScanCols * 128; e += 256) {
+      const int c = e & 127, vl = e >> 7;
+      if (v0 + vl < V && c < K) sin[(srow_s + v0 + vl) * K + c] = sS[c][vl];
+    }
     for (int e = tid; e < 128 * 128; e += 256) {
       const int c = e & 127, x = e >> 7;  // element (x, c) of the map tensor = M[c][x]
-      if (x < V && c < K) sin[(srow_s + x) * K + c] = sS[c * 129 + x];
-      sM[c * 129 + x] = (c < K && x < K) ? mmap[(mrow_s + x) * K + c] : 0.f;
+      sM[c][x] = (c < K && x < K) ? mmap[(mrow_s + x) * K + c] : 0.f;
     }
     __syncthreads();
-    float acc[8][8];
+    float acc[kScanCols / 2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int j = 0; j < kScanCols / 2; ++j) {
+      const int64_t v = v0 + j0 + j;
+      acc[j] = (r < K && v < V) ? bmap[(srow_s + v) * K + r] : 0.f;
+    }
+    if (r < K) {
+      for (int cp = 0; cp < K; ++cp) {
+        const float m = sM[r][cp];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int c = r0 + i, v = c0 + j;
-        acc[i][j] = (c < K && v < V) ? bmap[(srow_s + v) * K + c] : 0.f;
+        for (int j = 0; j < kScanCols / 2; ++j) acc[j] += m * sS[cp][j0 + j];
       }
-    for (int cp = 0; cp < K; ++cp) {
-      float mv[8], sv[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) mv[i] = sM[(r0 + i) * 129 + cp];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sv[j] = sS[cp * 129 + c0 + j];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] += mv[i] * sv[j];
     }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sS[(r0 + i) * 129 + c0 + j] = acc[i][j];
+    for (int j = 0; j < kScanCols / 2; ++j) sS[r][j0 + j] = acc[j];
     __syncthreads();
   }
   if (fin) {
-    for (int e = tid; e < 128 * 128; e += 256) {
-      const int c = e & 127, v = e >> 7;
-      if (c < K && v < V) {
-        const int64_t o = (srow + v) * K + c;
+    for (int e = tid; e < kScanCols * 128; e += 256) {
+      const int c = e & 127, vl = e >> 7;
+      if (c < K && v0 + vl < V) {
+        const int64_t o = (srow + v0 + vl) * K + c;
         if (fin_bf16)
-          static_cast<__bf16*>(fin)[o] = (__bf16)sS[c * 129 + v];
+          static_cast<__bf16*>(fin)[o] = (__bf16)sS[c][vl];
         else
-          static_cast<float*>(fin)[o] = sS[c * 129 + v];
+          static_cast<float*>(fin)[o] = sS[c][vl];
       }
     }
   }
@@ -1212,7 +1216,8 @@ hipError_t launch_chunk_prefill(const kda_prefill_args_t& a, hipStream_t stream)
     p2.fin = mmap;
     if ((e = launch_variant(p2, bf16, stream, true)) != hipSuccess) return e;
     // scan: S_in of every segment, final states
-    hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)(a.N * a.H)), dim3(256), 0, stream, sfirst, bmap, mmap,
+    const int64_t ncb = (a.V + kScanCols - 1) / kScanCols;
+    hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)(a.N * a.H * ncb)), dim3(256), 0, stream, sfirst, bmap, mmap,
                        a.initial_state, prm.init_bf16, a.final_state, prm.fin_bf16, sin, a.H, a.K, a.V);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // pass 2: outputs of every segment from its true initial state
