@@ -550,36 +550,47 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     float kx[RPW][CPL], qx[RPW][CPL], gx[RPW][CPL], vx[RPW][VPL], bt[RPW];
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
-      const bool okr = RPW * w + r < L;
-      bt[r] = okr ? __uint_as_float(raw.b[r]) : 0.f;
+      bt[r] = __uint_as_float(raw.b[r]);
 #pragma unroll
       for (int cc = 0; cc < CPL; ++cc) {
-        float kv, qv;
         if (kBF16 && CPL == 2) {
-          kv = __uint_as_float(cc == 0 ? raw.k[r][0] << 16 : raw.k[r][0] & 0xffff0000u);
-          qv = __uint_as_float(cc == 0 ? raw.q[r][0] << 16 : raw.q[r][0] & 0xffff0000u);
+          kx[r][cc] = __uint_as_float(cc == 0 ? raw.k[r][0] << 16 : raw.k[r][0] & 0xffff0000u);
+          qx[r][cc] = __uint_as_float(cc == 0 ? raw.q[r][0] << 16 : raw.q[r][0] & 0xffff0000u);
         } else if (kBF16) {
-          kv = __uint_as_float(raw.k[r][cc] << 16);
-          qv = __uint_as_float(raw.q[r][cc] << 16);
+          kx[r][cc] = __uint_as_float(raw.k[r][cc] << 16);
+          qx[r][cc] = __uint_as_float(raw.q[r][cc] << 16);
         } else {
-          kv = __uint_as_float(raw.k[r][cc]);
-          qv = __uint_as_float(raw.q[r][cc]);
+          kx[r][cc] = __uint_as_float(raw.k[r][cc]);
+          qx[r][cc] = __uint_as_float(raw.q[r][cc]);
         }
-        const bool okc = okr && c_lo + cc < K;
-        kx[r][cc] = okc ? kv : 0.f;
-        qx[r][cc] = okc ? qv : 0.f;
-        gx[r][cc] = okc ? raw.g[r][cc] : 0.f;
+        gx[r][cc] = raw.g[r][cc];
       }
 #pragma unroll
       for (int vv = 0; vv < VPL; ++vv) {
-        float x;
         if (kBF16 && VPL == 2)
-          x = __uint_as_float(vv == 0 ? raw.v[r][0] << 16 : raw.v[r][0] & 0xffff0000u);
+          vx[r][vv] = __uint_as_float(vv == 0 ? raw.v[r][0] << 16 : raw.v[r][0] & 0xffff0000u);
         else if (kBF16)
-          x = __uint_as_float(raw.v[r][vv] << 16);
+          vx[r][vv] = __uint_as_float(raw.v[r][vv] << 16);
         else
-          x = __uint_as_float(raw.v[r][vv]);
-        vx[r][vv] = (okr && vc_lo + vv < V && !p.v_zero) ? x : 0.f;
+          vx[r][vv] = __uint_as_float(raw.v[r][vv]);
+      }
+    }
+    // Rows past the chunk, channels past K and value columns past V were
+    // loaded clamped: zero them.  A full chunk has none (uniform branch).
+    if (!(L == kC && K == KP && v0 + BV <= V && !p.v_zero)) {
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        const bool okr = RPW * w + r < L;
+        bt[r] = okr ? bt[r] : 0.f;
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+          const bool okc = okr && c_lo + cc < K;
+          kx[r][cc] = okc ? kx[r][cc] : 0.f;
+          qx[r][cc] = okc ? qx[r][cc] : 0.f;
+          gx[r][cc] = okc ? gx[r][cc] : 0.f;
+        }
+#pragma unroll
+        for (int vv = 0; vv < VPL; ++vv) vx[r][vv] = (okr && vc_lo + vv < V && !p.v_zero) ? vx[r][vv] : 0.f;
       }
     }
     // (beta V)^T: this lane's RPW consecutive rows of each of its value columns
