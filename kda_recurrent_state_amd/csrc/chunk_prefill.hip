@@ -95,8 +95,12 @@ struct Cfg {
   static constexpr int R_KB = R_KE + SZ_KT;         // Kbar^T [KP][64]
   static constexpr int R_VT = R_KB + SZ_KT;         // (beta V)^T [BV][64]
   static constexpr int R_AB = R_VT + SZ_VT;         // bf16 [64][LDT]: -A_kk below the diagonal blocks, D_b on them
-  static constexpr int R_AD = R_AB + SZ_T;          // fp32 [4][16][17]: diagonal blocks of A_kk
-  static constexpr int R_AQK = R_AD + 4 * 16 * 17 * 4;  // A_qk bf16 [64][LDT]
+  // fp32 diagonal blocks of A_kk, column-major: element (row, col) of block b
+  // at b * AD_B + col * AD_C + row (16-byte aligned columns, blocks on
+  // different banks)
+  static constexpr int AD_C = 20, AD_B = 16 * AD_C + 4;
+  static constexpr int R_AD = R_AB + SZ_T;
+  static constexpr int R_AQK = R_AD + 4 * AD_B * 4;  // A_qk bf16 [64][LDT]
   static constexpr int R_TOT = R_AQK + SZ_T;        // per-wave gate sums fp32 [NW][KP]
   static constexpr int R_DEC = R_TOT + NW * KP * 4; // 2^gamma_L fp32 [KP]
   static constexpr int R_RED = R_DEC + KP * 4;      // range guard fp32 [NW]
@@ -764,10 +768,13 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
           for (int e = 0; e < 4; ++e) {
             const int row = 16 * bi + 4 * lg + e;
             sAqk[row * C::LDT + col] = (__bf16)(row >= col ? aqk[m][e] : 0.f);
-            if (bi == bj)
-              sAd[(bi * 16 + 4 * lg + e) * 17 + lr] = row > col ? akk[m][e] : 0.f;
-            else
-              sAb[row * C::LDT + col] = (__bf16)(-akk[m][e]);
+            if (bi != bj) sAb[row * C::LDT + col] = (__bf16)(-akk[m][e]);
+          }
+          if (bi == bj) {  // rows 4lg..4lg+3 of column lr: one 16-byte store
+            f32x4 d;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) d[e] = 4 * lg + e > lr ? akk[m][e] : 0.f;
+            *reinterpret_cast<f32x4*>(sAd + bi * C::AD_B + lr * C::AD_C + 4 * lg) = d;
           }
         }
       }
@@ -779,20 +786,30 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
 
     // ---------------- phase C: D_b = (I + A_bb)^-1 for the diagonal blocks --
     if (w == 0) {
-      // fp32 substitution; lane = (block, column); result stored as bf16
+      // fp32 forward substitution; lane = (block, column).  Step j needs
+      // column j of the block: four 16-byte reads, issued one step ahead.
       const int bb = l >> 4;
       int col = l & 15;
       asm volatile("" : "+v"(col));  // keep the identity column below from being hoisted out of the chunk loop
-      const float* Ab = sAd + bb * 16 * 17;
+      const f32x4* Ab = reinterpret_cast<const f32x4*>(sAd + bb * C::AD_B);
       float x[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) x[i] = (i == col) ? 1.f : 0.f;
+      f32x4 cur[4], nxt[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) cur[q] = Ab[q];  // column 0
 #pragma unroll
       for (int j = 0; j < 15; ++j) {
+        if (j < 14) {
 #pragma unroll
-        for (int i = j + 1; i < 16; ++i) x[i] -= Ab[i * 17 + j] * x[j];
-        // bound how many triangle reads the scheduler hoists (register pressure)
-        if (j % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+          for (int q = 0; q < 4; ++q)
+            if (4 * q + 3 > j + 1) nxt[q] = Ab[(j + 1) * (C::AD_C / 4) + q];
+        }
+#pragma unroll
+        for (int i = j + 1; i < 16; ++i) x[i] -= cur[i >> 2][i & 3] * x[j];
+        __builtin_amdgcn_sched_barrier(0);  // one column in flight at a time (register pressure)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cur[q] = nxt[q];
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) sAb[(16 * bb + i) * C::LDT + 16 * bb + col] = (__bf16)x[i];
