@@ -127,7 +127,8 @@ kda_status_t kda_state_scatter(const kda_state_cache_t* cache, const void* indic
 /*
  * Arguments of kda_chunk_prefill.  All pointers are device pointers to
  * contiguous row-major arrays.
- *  T, N, H, K, V   -- tokens, sequences, heads, key dim (1..128), value dim (>= 1).
+ *  T, N, H, K, V   -- tokens, sequences, heads, key dim (1..128), value dim (>= 1);
+ *                     H * max(K, V) <= 2^22 (else KDA_E_UNSUPPORTED).
  *  q, k            -- [T, H, K] in qkv_dtype.           v -- [T, H, V] in qkv_dtype.
  *  g               -- [T, H, K] fp32: natural-log decay per key channel; the
  *                     state is multiplied by exp(g) (g <= 0 for a decay).

@@ -112,6 +112,13 @@ struct Cfg {
 
 __device__ __forceinline__ float bf2f(unsigned short u) { return __uint_as_float((unsigned)u << 16); }
 
+// A T at a 32-bit byte offset from a uniform base (lets the compiler use the
+// scalar-base + 32-bit vector-offset addressing form).
+template <typename T>
+__device__ __forceinline__ T ld_at(const char* base, uint32_t off) {
+  return *reinterpret_cast<const T*>(base + off);
+}
+
 template <bool kBF16>
 __device__ __forceinline__ float ld_in(const void* p, int64_t i) {
   if (kBF16) return bf2f(static_cast<const unsigned short*>(p)[i]);
@@ -406,68 +413,84 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
   const int64_t vstride = p.v_zero ? K : V;
   auto issue_loads = [&](int64_t tb) {
     const int64_t span = (len - tb) < (int64_t)kC ? (len - tb) : (int64_t)kC;
-    int64_t th[RPW];
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      const int i = RPW * w + r;
-      th[r] = (bos + tb + (i < span ? i : span - 1)) * H + h;
-    }
-    if (p.beta_bf16) {
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) raw.b[r] = (unsigned)static_cast<const unsigned short*>(p.beta)[th[r]] << 16;
-    } else {
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) raw.b[r] = static_cast<const unsigned*>(p.beta)[th[r]];
-    }
     if (p.pair) {
-      // two key channels (CPL == 2) / value columns (VPL == 2) per access
-      const int64_t cs = CPL == 2 ? (c_lo + 1 < K ? c_lo : K - 2) : (c_lo < K ? c_lo : K - 1);
-      const int64_t vs = VPL == 2 ? (vc_lo + 1 < V ? vc_lo : V - 2) : (vc_lo < V ? vc_lo : V - 1);
+      // Uniform 64-bit bases at the chunk's first (token, head) row and
+      // 32-bit offsets from them (H * max(K, V) <= 2^22 keeps a chunk's
+      // offsets below 2^31 bytes); two key channels (CPL == 2) / value
+      // columns (VPL == 2) per access.
+      constexpr uint32_t eb = kBF16 ? 2 : 4;
+      const int64_t row0 = (bos + tb) * H + h;
+      const char* kb = static_cast<const char*>(p.k) + row0 * K * eb;
+      const char* qb = static_cast<const char*>(p.q) + row0 * K * eb;
+      const char* vb = static_cast<const char*>(vsrc) + row0 * vstride * eb;
+      const char* gb = reinterpret_cast<const char*>(p.g) + row0 * K * 4;
+      const char* bb = static_cast<const char*>(p.beta) + row0 * (p.beta_bf16 ? 2 : 4);
+      const uint32_t cs = (uint32_t)(CPL == 2 ? (c_lo + 1 < K ? c_lo : K - 2) : (c_lo < K ? c_lo : K - 1));
+      const uint32_t vs = (uint32_t)(VPL == 2 ? (vc_lo + 1 < V ? vc_lo : V - 2) : (vc_lo < V ? vc_lo : V - 1));
+      uint32_t ri[RPW];  // (token, head) rows after row0, clamped to the span
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
+        const int i = RPW * w + r;
+        ri[r] = (uint32_t)((i < span ? i : span - 1) * H);
+      }
+      if (p.beta_bf16) {
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) raw.b[r] = (unsigned)ld_at<unsigned short>(bb, 2 * ri[r]) << 16;
+      } else {
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) raw.b[r] = ld_at<unsigned>(bb, 4 * ri[r]);
+      }
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        const uint32_t ek = ri[r] * (uint32_t)K + cs;        // element offset in k, q, g
+        const uint32_t ev = ri[r] * (uint32_t)vstride + vs;  // element offset in v
         if (kBF16) {
-          const unsigned short* k16 = static_cast<const unsigned short*>(p.k) + th[r] * K + cs;
-          const unsigned short* q16 = static_cast<const unsigned short*>(p.q) + th[r] * K + cs;
-          const unsigned short* v16 = static_cast<const unsigned short*>(vsrc) + th[r] * vstride + vs;
           if (CPL == 2) {
-            raw.k[r][0] = *reinterpret_cast<const unsigned*>(k16);
-            raw.q[r][0] = *reinterpret_cast<const unsigned*>(q16);
+            raw.k[r][0] = ld_at<unsigned>(kb, 2 * ek);
+            raw.q[r][0] = ld_at<unsigned>(qb, 2 * ek);
           } else {
-            raw.k[r][0] = *k16;
-            raw.q[r][0] = *q16;
+            raw.k[r][0] = ld_at<unsigned short>(kb, 2 * ek);
+            raw.q[r][0] = ld_at<unsigned short>(qb, 2 * ek);
           }
-          if (VPL == 2)
-            raw.v[r][0] = *reinterpret_cast<const unsigned*>(v16);
-          else
-            raw.v[r][0] = *v16;
+          raw.v[r][0] = VPL == 2 ? ld_at<unsigned>(vb, 2 * ev) : (unsigned)ld_at<unsigned short>(vb, 2 * ev);
         } else {
-          const unsigned* k32 = static_cast<const unsigned*>(p.k) + th[r] * K + cs;
-          const unsigned* q32 = static_cast<const unsigned*>(p.q) + th[r] * K + cs;
-          const unsigned* v32 = static_cast<const unsigned*>(vsrc) + th[r] * vstride + vs;
           if (CPL == 2) {
-            const uint2 a = *reinterpret_cast<const uint2*>(k32), c = *reinterpret_cast<const uint2*>(q32);
+            const uint2 a = ld_at<uint2>(kb, 4 * ek), c = ld_at<uint2>(qb, 4 * ek);
             raw.k[r][0] = a.x; raw.k[r][CPL - 1] = a.y;
             raw.q[r][0] = c.x; raw.q[r][CPL - 1] = c.y;
           } else {
-            raw.k[r][0] = *k32;
-            raw.q[r][0] = *q32;
+            raw.k[r][0] = ld_at<unsigned>(kb, 4 * ek);
+            raw.q[r][0] = ld_at<unsigned>(qb, 4 * ek);
           }
           if (VPL == 2) {
-            const uint2 a = *reinterpret_cast<const uint2*>(v32);
+            const uint2 a = ld_at<uint2>(vb, 4 * ev);
             raw.v[r][0] = a.x; raw.v[r][VPL - 1] = a.y;
           } else {
-            raw.v[r][0] = *v32;
+            raw.v[r][0] = ld_at<unsigned>(vb, 4 * ev);
           }
         }
         if (CPL == 2) {
-          const float2 fg = *reinterpret_cast<const float2*>(p.g + th[r] * K + cs);
+          const float2 fg = ld_at<float2>(gb, 4 * ek);
           raw.g[r][0] = fg.x;
           raw.g[r][CPL - 1] = fg.y;
         } else {
-          raw.g[r][0] = p.g[th[r] * K + cs];
+          raw.g[r][0] = ld_at<float>(gb, 4 * ek);
         }
       }
     } else {
+      int64_t th[RPW];
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        const int i = RPW * w + r;
+        th[r] = (bos + tb + (i < span ? i : span - 1)) * H + h;
+      }
+      if (p.beta_bf16) {
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) raw.b[r] = (unsigned)static_cast<const unsigned short*>(p.beta)[th[r]] << 16;
+      } else {
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) raw.b[r] = static_cast<const unsigned*>(p.beta)[th[r]];
+      }
       // element by element (odd K or V, or unaligned tensors); bf16 pairs are
       // packed after the loads return
 #pragma unroll

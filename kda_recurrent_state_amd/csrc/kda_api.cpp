@@ -127,6 +127,7 @@ kda_status_t kda_chunk_prefill(const kda_prefill_args_t* a, void* stream) {
   if (a->initial_state && !valid_dtype(a->initial_dtype)) return KDA_E_DTYPE;
   if (a->final_state && !valid_dtype(a->final_dtype)) return KDA_E_DTYPE;
   if (a->K > 128) return KDA_E_UNSUPPORTED;
+  if (a->H * (a->K > a->V ? a->K : a->V) > ((int64_t)1 << 22)) return KDA_E_UNSUPPORTED;  // 32-bit chunk offsets
   if (a->ckpt_states) {
     if (a->ckpt_interval <= 0 || a->ckpt_interval % 64 != 0 || a->num_ckpt < 0) return KDA_E_SHAPE;
     if (!a->ckpt_cu) return KDA_E_NULL;

@@ -117,7 +117,7 @@ def _args(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(K=0), 3), (dict(V=0), 3), (dict(H=0), 3), (dict(T=-1), 3), (dict(N=-1), 3),
     (dict(N=0, T=5), 3),
-    (dict(K=129), 6),
+    (dict(K=129), 6), (dict(H=1 << 20), 6),     # H * max(K, V) above 2^22
     (dict(qkv_dtype=3), 2), (dict(beta_dtype=9), 2),
     (dict(cu_seqlens=0), 1), (dict(q=0), 1), (dict(g=0), 1), (dict(out=0), 1),
     (dict(N=4, workspace=0, workspace_bytes=0), 7),
