@@ -667,14 +667,17 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
 #pragma unroll
     for (int cc = 0; cc < CPL; ++cc) {
       const int64_t c = c_lo + cc;
-      float off = 0.f, ref = 0.f, tot = 0.f;
+      // prefix sums of the wave totals: off = before this wave, ref = before
+      // the reference row, tot = the whole chunk (w and mw are uniform)
+      float pre[NW + 1];
+      pre[0] = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) {
-        const float x = sTot[ww * KP + c];
-        off += ww < w ? x : 0.f;
-        ref += ww < mw ? x : 0.f;
-        tot += x;
-      }
+      for (int ww = 0; ww < NW; ++ww) pre[ww + 1] = pre[ww] + sTot[ww * KP + c];
+      const float tot = pre[NW];
+      const float ref = mw == 32 / RPW ? pre[32 / RPW] : pre[16 / RPW];
+      float off = pre[0];
+#pragma unroll
+      for (int ww = 1; ww < NW; ++ww) off = w == ww ? pre[ww] : off;
       gm[cc] = ref * kLog2e;
       gL[cc] = tot * kLog2e;
 #pragma unroll
@@ -708,19 +711,23 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
         const int i = RPW * w + r;
+        const float bk = bt[r] * rk[r];   // beta / |k| of this row
+        const float sq = scale * rq[r];   // scale / |q|
         __bf16 kl[CPL], ql[CPL], kr[CPL], qg[CPL];
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) {
-          const float e1 = __builtin_amdgcn_exp2f(gx[r][cc] - gm[cc]);  // 2^(gamma_i - gamma_m)
-          const float e2 = __builtin_amdgcn_exp2f(gm[cc] - gx[r][cc]);  // 2^(gamma_m - gamma_i)
-          const float kh = kx[r][cc] * rk[r];
-          const float qh = qx[r][cc] * rq[r];
-          kl[cc] = (__bf16)(bt[r] * kh * e1);
-          ql[cc] = (__bf16)(scale * qh * e1);
-          kr[cc] = (__bf16)(kh * e2);
-          qg[cc] = (__bf16)(scale * qh * (e1 * cg[cc]));
-          ke[cc][r] = (__bf16)(bt[r] * kh * (e1 * cg[cc]));
-          kb[cc][r] = (__bf16)(kh * (e2 * cb[cc]));
+          const float d = gx[r][cc] - gm[cc];
+          const float e1 = __builtin_amdgcn_exp2f(d);   // 2^(gamma_i - gamma_m)
+          const float e2 = __builtin_amdgcn_exp2f(-d);  // 2^(gamma_m - gamma_i)
+          const float fkl = kx[r][cc] * e1 * bk;        // beta k^ 2^(gamma_i - gamma_m)
+          const float fql = qx[r][cc] * e1 * sq;        // scale q^ 2^(gamma_i - gamma_m)
+          const float fkr = kx[r][cc] * e2 * rk[r];     // k^ 2^(gamma_m - gamma_i)
+          kl[cc] = (__bf16)fkl;
+          ql[cc] = (__bf16)fql;
+          kr[cc] = (__bf16)fkr;
+          qg[cc] = (__bf16)(fql * cg[cc]);              // scale q^ 2^gamma_i
+          ke[cc][r] = (__bf16)(fkl * cg[cc]);           // beta k^ 2^gamma_i
+          kb[cc][r] = (__bf16)(fkr * cb[cc]);           // k^ 2^(gamma_L - gamma_i)
         }
         if (CPL == 2) {
           typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
