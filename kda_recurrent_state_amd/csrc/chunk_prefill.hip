@@ -922,6 +922,9 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) bV[q2] = pack_perm(Vn[2 * q2], Vn[2 * q2 + 1]);
     __builtin_amdgcn_sched_barrier(0);
+    // The output is computed transposed, O^T = S^T Qg^T + V_new^T A_qk^T (the
+    // operands of each product swapped): tile rt then holds, per lane, the
+    // four consecutive value columns 16w + 4lg.. of token 16rt + lr.
     f32x4 O[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) O[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -931,14 +934,14 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) a[rt] = ld_perm(sQg + (16 * rt + lr) * C::LDKE + 32 * ks + 4 * lg);
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) O[rt] = mfma(a[rt], bS[ks], O[rt]);
+      for (int rt = 0; rt < 4; ++rt) O[rt] = mfma(bS[ks], a[rt], O[rt]);
     }
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         if (32 * q2 > 16 * rt + 15) continue;
-        O[rt] = mfma(ld_perm(sAqk + (16 * rt + lr) * C::LDT + 32 * q2 + 4 * lg), bV[q2], O[rt]);
+        O[rt] = mfma(bV[q2], ld_perm(sAqk + (16 * rt + lr) * C::LDT + 32 * q2 + 4 * lg), O[rt]);
       }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -953,11 +956,12 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     if (p.out == nullptr) {
       // maps of a segment only (no outputs)
     } else if (kBF16 && p.ovec) {
-      // stage through LDS (KR is dead) and store whole 16-byte runs of rows
+      // stage through LDS (KR is dead), one 8-byte write per tile, and store
+      // whole 16-byte runs of rows
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sO[(16 * rt + 4 * lg + e) * C::LDO + 16 * w + lr] = (__bf16)O[rt][e];
+        *reinterpret_cast<bf16x4*>(sO + (16 * rt + lr) * C::LDO + 16 * w + 4 * lg) =
+            bf16x4{(__bf16)O[rt][0], (__bf16)O[rt][1], (__bf16)O[rt][2], (__bf16)O[rt][3]};
       lds_barrier();
       constexpr int VPR = BV / 8;  // 16-byte runs per row
 #pragma unroll
@@ -969,20 +973,22 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
           *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(p.out) + o) = ld8(sO + i * C::LDO + 8 * cv);
         }
       }
-    } else if (vcol < V) {
+    } else {
+      const int64_t vb = v0 + 16 * w + 4 * lg;  // this lane's first output column
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
+      for (int rt = 0; rt < 4; ++rt) {
+        const int i = 16 * rt + lr;
+        if (i >= L) continue;
+        const int64_t o = ((bos + t0 + i) * H + h) * V + vb;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int i = 16 * rt + 4 * lg + e;
-          if (i < L) {
-            const int64_t o = ((bos + t0 + i) * H + h) * V + vcol;
-            if (kBF16)
-              static_cast<__bf16*>(p.out)[o] = (__bf16)O[rt][e];
-            else
-              static_cast<float*>(p.out)[o] = O[rt][e];
-          }
+          if (vb + e >= V) continue;
+          if (kBF16)
+            static_cast<__bf16*>(p.out)[o + e] = (__bf16)O[rt][e];
+          else
+            static_cast<float*>(p.out)[o + e] = O[rt][e];
         }
+      }
     }
     t0 += L;
     Lcap = kC;
