@@ -602,8 +602,29 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
           vx[r][vv] = __uint_as_float(raw.v[r][vv]);
       }
     }
+    // squared row norms of k and q (bf16 pairs: one dot2 per pair)
+    float sk[RPW], sq[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      if (kBF16 && CPL == 2) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        sk[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, raw.k[r][0]),
+                                                __builtin_bit_cast(bf16x2, raw.k[r][0]), 0.f, false);
+        sq[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, raw.q[r][0]),
+                                                __builtin_bit_cast(bf16x2, raw.q[r][0]), 0.f, false);
+      } else {
+        sk[r] = 0.f;
+        sq[r] = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+          sk[r] += kx[r][cc] * kx[r][cc];
+          sq[r] += qx[r][cc] * qx[r][cc];
+        }
+      }
+    }
     // Rows past the chunk, channels past K and value columns past V were
-    // loaded clamped: zero them.  A full chunk has none (uniform branch).
+    // loaded clamped: zero them (and redo the norms).  A full chunk has none
+    // (uniform branch).
     if (!(L == kC && K == KP && v0 + BV <= V && !p.v_zero)) {
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
@@ -618,6 +639,13 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
         }
 #pragma unroll
         for (int vv = 0; vv < VPL; ++vv) vx[r][vv] = (okr && vc_lo + vv < V && !p.v_zero) ? vx[r][vv] : 0.f;
+        sk[r] = 0.f;
+        sq[r] = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+          sk[r] += kx[r][cc] * kx[r][cc];
+          sq[r] += qx[r][cc] * qx[r][cc];
+        }
       }
     }
     // (beta V)^T: this lane's RPW consecutive rows of each of its value columns
@@ -647,16 +675,10 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     float rk[RPW], rq[RPW];
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
-      float sk = 0.f, sq = 0.f;
-#pragma unroll
-      for (int cc = 0; cc < CPL; ++cc) {
-        sk += kx[r][cc] * kx[r][cc];
-        sq += qx[r][cc] * qx[r][cc];
-      }
-      sk = wave_sum(sk);
-      sq = wave_sum(sq);
-      rk[r] = p.l2norm ? __frsqrt_rn(sk + kL2Eps) : 1.f;
-      rq[r] = p.l2norm ? __frsqrt_rn(sq + kL2Eps) : 1.f;
+      const float tk = wave_sum(sk[r]);
+      const float tq = wave_sum(sq[r]);
+      rk[r] = p.l2norm ? __frsqrt_rn(tk + kL2Eps) : 1.f;
+      rq[r] = p.l2norm ? __frsqrt_rn(tq + kL2Eps) : 1.f;
     }
     lds_barrier();
 
@@ -688,15 +710,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
       guard = fmaxf(guard, fmaxf(gm[cc], gL[cc] - gm[cc]));
     }
     guard = wave_max(guard);
-    if (l == 0) sRed[w] = guard;
-    lds_barrier();
-    float gmax = sRed[0];
-#pragma unroll
-    for (int ww = 1; ww < NW; ++ww) gmax = fmaxf(gmax, sRed[ww]);
-    if (gmax > kRangeLimit && L > 1) {
-      Lcap = L > 16 ? 16 : (L > 4 ? 4 : 1);
-      continue;  // re-process this span as shorter chunks
-    }
+    if (l == 0) sRed[w] = guard;  // checked after phase A's barrier
 
     // ---------------- phase A: gated operand tiles into LDS ----------------
     {
@@ -761,6 +775,18 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
       }
     }
     lds_barrier();
+    {
+      // range guard of every wave (written before the barrier above): a span
+      // whose gate factors would leave 2^+-100 is re-processed as shorter
+      // chunks, discarding this pass's tiles
+      float gmax = sRed[0];
+#pragma unroll
+      for (int ww = 1; ww < NW; ++ww) gmax = fmaxf(gmax, sRed[ww]);
+      if (gmax > kRangeLimit && L > 1) {
+        Lcap = L > 16 ? 16 : (L > 4 ? 4 : 1);
+        continue;
+      }
+    }
 
     // ---------------- phase B: A_kk (fp32) and A_qk (bf16) -----------------
     // 10 lower 16x16 block pairs (bi >= bj), round-robin over waves; A_kk and
