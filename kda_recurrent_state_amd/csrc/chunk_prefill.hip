@@ -137,20 +137,33 @@ __device__ __forceinline__ float lane_f(float x, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }
 
+// DPP move of x from the lanes named by kCtrl into the rows of kRowMask; the
+// other rows get 0.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_rows(float x) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, kRowMask, 0xF, false));
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
   x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
   x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
   x += dpp<0x141>(x);  // row_half_mirror
-  x += dpp<0x140>(x);  // row_mirror
-  return (lane_f(x, 0) + lane_f(x, 16)) + (lane_f(x, 32) + lane_f(x, 48));
+  x += dpp<0x140>(x);  // row_mirror: every lane of a row holds the row sum
+  x += dpp_rows<0x142, 0xA>(x);  // row_bcast:15: rows 1, 3 add rows 0, 2
+  x += dpp_rows<0x143, 0xC>(x);  // row_bcast:31: rows 2, 3 add rows 0 + 1
+  return lane_f(x, 63);
 }
 
+// (for x >= 0: rows outside the broadcast masks receive 0)
 __device__ __forceinline__ float wave_max(float x) {
   x = fmaxf(x, dpp<0xB1>(x));
   x = fmaxf(x, dpp<0x4E>(x));
   x = fmaxf(x, dpp<0x141>(x));
   x = fmaxf(x, dpp<0x140>(x));
-  return fmaxf(fmaxf(lane_f(x, 0), lane_f(x, 16)), fmaxf(lane_f(x, 32), lane_f(x, 48)));
+  x = fmaxf(x, dpp_rows<0x142, 0xA>(x));
+  x = fmaxf(x, dpp_rows<0x143, 0xC>(x));
+  return lane_f(x, 63);
 }
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -671,14 +684,17 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
       }
       sTot[w * KP + c_lo + cc] = run;
     }
-    // 1 / |row| for q and k
+    // 1 / |row| for q and k (1 without l2norm; uniform branch)
     float rk[RPW], rq[RPW];
+    if (p.l2norm) {
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      const float tk = wave_sum(sk[r]);
-      const float tq = wave_sum(sq[r]);
-      rk[r] = p.l2norm ? __frsqrt_rn(tk + kL2Eps) : 1.f;
-      rq[r] = p.l2norm ? __frsqrt_rn(tq + kL2Eps) : 1.f;
+      for (int r = 0; r < RPW; ++r) {
+        rk[r] = __frsqrt_rn(wave_sum(sk[r]) + kL2Eps);
+        rq[r] = __frsqrt_rn(wave_sum(sq[r]) + kL2Eps);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) rk[r] = rq[r] = 1.f;
     }
     lds_barrier();
 
