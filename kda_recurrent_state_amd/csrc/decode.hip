@@ -82,6 +82,18 @@ template <typename T>
 __device__ __forceinline__ void sto(void* base, uint32_t off, T x) {
   *reinterpret_cast<T*>(static_cast<char*>(base) + off) = x;
 }
+typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+// Streamed (non-temporal) state traffic: each row is read and written once.
+template <typename T>
+__device__ __forceinline__ T ldo_nt(const void* base, uint32_t off) {
+  return __builtin_nontemporal_load(reinterpret_cast<const T*>(static_cast<const char*>(base) + off));
+}
+template <typename T>
+__device__ __forceinline__ void sto_nt(void* base, uint32_t off, T x) {
+  __builtin_nontemporal_store(x, reinterpret_cast<T*>(static_cast<char*>(base) + off));
+}
 
 // Raw words of EPL state elements: EPL/2 words for bf16, EPL for fp32.
 template <int EPL, bool kSB>
@@ -99,12 +111,12 @@ __device__ __forceinline__ void load_words(const char* base, uint32_t off, int j
   if constexpr (kVec) {
     const uint32_t o = off + 4u * W * (uint32_t)j;
     if constexpr (W == 2) {
-      const uint2 a = ldo<uint2>(base, o);
+      const u32x2v a = ldo_nt<u32x2v>(base, o);
       r.w[0] = a.x; r.w[1] = a.y;
     } else {
 #pragma unroll
       for (int i = 0; i < W; i += 4) {
-        const uint4 a = ldo<uint4>(base, o + 4u * i);
+        const u32x4v a = ldo_nt<u32x4v>(base, o + 4u * i);
         r.w[i] = a.x; r.w[i + 1] = a.y; r.w[i + 2] = a.z; r.w[i + 3] = a.w;
       }
     }
@@ -142,11 +154,11 @@ __device__ __forceinline__ void store_row(char* base, uint32_t off, int j, int K
       bfv o;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) o[e] = (__bf16)x[e];
-      sto<bfv>(base, off + 2u * EPL * (uint32_t)j, o);
+      sto_nt<bfv>(base, off + 2u * EPL * (uint32_t)j, o);
     } else {
 #pragma unroll
       for (int i = 0; i < EPL; i += 4)
-        sto<float4>(base, off + 4u * (EPL * (uint32_t)j + i), float4{x[i], x[i + 1], x[i + 2], x[i + 3]});
+        sto_nt<f32x4v>(base, off + 4u * (EPL * (uint32_t)j + i), f32x4v{x[i], x[i + 1], x[i + 2], x[i + 3]});
     }
   } else {
 #pragma unroll

@@ -19,8 +19,11 @@
 // One workgroup per (selected state, head).  Quantize: 16 lanes per row, each
 // holding 8 consecutive channels; 16 row groups; the rows stay in registers
 // (up to 128) between the column-max pass and the encode pass, so the source
-// is read once.  Dequantize: 16 lanes per row, 8 channels per lane, the code
-// loads of 8 rows issued before their conversion and stores.
+// is read once.  Dequantize: 16 lanes per row, each holding 4 channels at c
+// and 4 at c + 64, so that every store instruction of a row writes one
+// contiguous run; the code loads of 8 rows are issued before their
+// conversion and stores.  State rows and codes are streamed with
+// non-temporal loads and stores.
 #include "internal.h"
 
 namespace kda {
@@ -64,6 +67,19 @@ __device__ __forceinline__ int encode(float x, float sc) {
   return (int)r;
 }
 
+typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+// Streamed (non-temporal) accesses: state rows and codes are touched once.
+template <typename T>
+__device__ __forceinline__ T ld_nt(const void* p) {
+  return __builtin_nontemporal_load(static_cast<const T*>(p));
+}
+template <typename T>
+__device__ __forceinline__ void st_nt(void* p, T x) {
+  __builtin_nontemporal_store(x, static_cast<T*>(p));
+}
+
 // kKeep: V <= kQGroups * kQRows, rows held in registers; else the encode pass
 // reads the rows again.
 template <bool kKeep>
@@ -86,14 +102,17 @@ __global__ __launch_bounds__(kQThreads) void quantize_scatter_kernel(Int8Params 
     const int64_t e = src + (int64_t)row * K + c0;
     if (p.vec) {
       if (p.pbf16) {
-        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const unsigned short*>(p.packed) + e);
+        const u32x4v u = kKeep ? ld_nt<u32x4v>(static_cast<const unsigned short*>(p.packed) + e)
+                               : *reinterpret_cast<const u32x4v*>(static_cast<const unsigned short*>(p.packed) + e);
         const unsigned w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
         for (int t = 0; t < kQC; ++t)
           x[t] = (t & 1) ? __uint_as_float(w[t >> 1] & 0xffff0000u) : __uint_as_float(w[t >> 1] << 16);
       } else {
-        const float4 f0 = *reinterpret_cast<const float4*>(static_cast<const float*>(p.packed) + e);
-        const float4 f1 = *reinterpret_cast<const float4*>(static_cast<const float*>(p.packed) + e + 4);
+        const f32x4v f0 = kKeep ? ld_nt<f32x4v>(static_cast<const float*>(p.packed) + e)
+                                : *reinterpret_cast<const f32x4v*>(static_cast<const float*>(p.packed) + e);
+        const f32x4v f1 = kKeep ? ld_nt<f32x4v>(static_cast<const float*>(p.packed) + e + 4)
+                                : *reinterpret_cast<const f32x4v*>(static_cast<const float*>(p.packed) + e + 4);
         x[0] = f0.x; x[1] = f0.y; x[2] = f0.z; x[3] = f0.w;
         x[4] = f1.x; x[5] = f1.y; x[6] = f1.z; x[7] = f1.w;
       }
@@ -153,7 +172,7 @@ __global__ __launch_bounds__(kQThreads) void quantize_scatter_kernel(Int8Params 
       unsigned w[2] = {0u, 0u};
 #pragma unroll
       for (int t = 0; t < kQC; ++t) w[t >> 2] |= (unsigned)(qq[t] & 0xff) << (8 * (t & 3));
-      *reinterpret_cast<uint2*>(dst) = uint2{w[0], w[1]};
+      st_nt<u32x2v>(dst, u32x2v{w[0], w[1]});
     } else {
 #pragma unroll
       for (int t = 0; t < kQC; ++t)
@@ -177,31 +196,6 @@ __global__ __launch_bounds__(kQThreads) void quantize_scatter_kernel(Int8Params 
 
 constexpr int kDRows = 8;  // rows per thread per batch, dequantize (loads issued together)
 
-__device__ __forceinline__ void store8(void* packed, int bf, int vec, int64_t e, int c0, int K, const float (&x)[8]) {
-  if (vec) {
-    if (bf) {
-      typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
-      bf8 o;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) o[t] = (__bf16)x[t];
-      *reinterpret_cast<bf8*>(static_cast<__bf16*>(packed) + e) = o;
-    } else {
-      float* d = static_cast<float*>(packed) + e;
-      *reinterpret_cast<float4*>(d) = float4{x[0], x[1], x[2], x[3]};
-      *reinterpret_cast<float4*>(d + 4) = float4{x[4], x[5], x[6], x[7]};
-    }
-  } else {
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      if (c0 + t >= K) continue;
-      if (bf)
-        static_cast<__bf16*>(packed)[e + t] = (__bf16)x[t];
-      else
-        static_cast<float*>(packed)[e + t] = x[t];
-    }
-  }
-}
-
 __global__ __launch_bounds__(kQThreads) void dequantize_gather_kernel(Int8Params p) {
   const int64_t i = blockIdx.x / p.H;
   const int64_t h = blockIdx.x - i * p.H;
@@ -213,40 +207,73 @@ __global__ __launch_bounds__(kQThreads) void dequantize_gather_kernel(Int8Params
   const int64_t dst = (i * p.H + h) * p.V * p.K;  // element offset of the packed slice
   const int8_t* qs = take ? p.q + slot * p.qs0 + h * p.V * p.K : nullptr;
   const float* ss = take ? p.s + slot * p.ss0 + h * p.K : nullptr;
+  if (p.vec) {
+    // groups of 4 channels at ca and ca + 64: each store instruction of a
+    // row's 16 lanes covers one contiguous run
+    for (int cb = 0; cb < K; cb += 8 * kDLanes) {
+      const int ca = cb + 4 * lane, cc = ca + 4 * kDLanes;
+      if (ca >= K) continue;
+      const bool hc = cc < K;
+      float sc[8];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        sc[t] = take ? ss[ca + t] : 0.f;
+        sc[4 + t] = take && hc ? ss[cc + t] : 0.f;
+      }
+      for (int r0 = grp; r0 < V; r0 += kDGroups * kDRows) {
+        unsigned ua[kDRows], uc[kDRows];
+        if (take) {
+#pragma unroll
+          for (int r = 0; r < kDRows; ++r) {
+            int row = r0 + kDGroups * r;
+            row = row < V ? row : V - 1;
+            ua[r] = ld_nt<unsigned>(qs + (int64_t)row * K + ca);
+            uc[r] = hc ? ld_nt<unsigned>(qs + (int64_t)row * K + cc) : 0u;
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < kDRows; ++r) {
+          const int row = r0 + kDGroups * r;
+          if (row >= V) break;
+          float x[8];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            x[t] = take ? (float)(int8_t)((ua[r] >> (8 * t)) & 0xff) * sc[t] : 0.f;
+            x[4 + t] = take ? (float)(int8_t)((uc[r] >> (8 * t)) & 0xff) * sc[4 + t] : 0.f;
+          }
+          const int64_t e = dst + (int64_t)row * K;
+          if (p.pbf16) {
+            typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
+            __bf16* d = static_cast<__bf16*>(p.packed) + e;
+            st_nt<bf4>(d + ca, bf4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]});
+            if (hc) st_nt<bf4>(d + cc, bf4{(__bf16)x[4], (__bf16)x[5], (__bf16)x[6], (__bf16)x[7]});
+          } else {
+            float* d = static_cast<float*>(p.packed) + e;
+            st_nt<f32x4v>(d + ca, f32x4v{x[0], x[1], x[2], x[3]});
+            if (hc) st_nt<f32x4v>(d + cc, f32x4v{x[4], x[5], x[6], x[7]});
+          }
+        }
+      }
+    }
+    return;
+  }
+  // element path (K not a multiple of 8 or unaligned rows): lane covers 8 channels
   for (int cb = 0; cb < K; cb += 8 * kDLanes) {
     const int c0 = cb + 8 * lane;
     if (c0 >= K) continue;
     float sc[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) sc[t] = (take && c0 + t < K) ? ss[c0 + t] : 0.f;
-    for (int r0 = grp; r0 < V; r0 += kDGroups * kDRows) {
-      // every code load of the batch first
-      uint2 u[kDRows];
-      if (take && p.vec) {
+    for (int row = grp; row < V; row += kDGroups) {
+      const int64_t e = dst + (int64_t)row * K + c0;
 #pragma unroll
-        for (int r = 0; r < kDRows; ++r) {
-          int row = r0 + kDGroups * r;
-          row = row < V ? row : V - 1;
-          u[r] = *reinterpret_cast<const uint2*>(qs + (int64_t)row * K + c0);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < kDRows; ++r) {
-        const int row = r0 + kDGroups * r;
-        if (row >= V) break;
-        float x[8];
-        if (take && p.vec) {
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const unsigned w = t < 4 ? u[r].x : u[r].y;
-            x[t] = (float)(int8_t)((w >> (8 * (t & 3))) & 0xff) * sc[t];
-          }
-        } else {
-#pragma unroll
-          for (int t = 0; t < 8; ++t)
-            x[t] = (take && c0 + t < K) ? (float)qs[(int64_t)row * K + c0 + t] * sc[t] : 0.f;
-        }
-        store8(p.packed, p.pbf16, p.vec, dst + (int64_t)row * K + c0, c0, K, x);
+      for (int t = 0; t < 8; ++t) {
+        if (c0 + t >= K) continue;
+        const float x = take ? (float)qs[(int64_t)row * K + c0 + t] * sc[t] : 0.f;
+        if (p.pbf16)
+          static_cast<__bf16*>(p.packed)[e + t] = (__bf16)x;
+        else
+          static_cast<float*>(p.packed)[e + t] = x;
       }
     }
   }
