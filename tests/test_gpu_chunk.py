@@ -2,8 +2,10 @@
 
 Small cases are compared over every element; they span several chunks and
 tiles, ragged tails, K != V, V-split blocks, zero-length sequences, fp32 and
-bf16 I/O, no initial state, bf16 final states, out aliasing v, strong decays
-that force shorter chunks, split/resume and determinism.
+bf16 I/O, vector and element-by-element loads (odd K or V, sizes that are not
+a multiple of 4, unaligned tensors), no initial state, bf16 final states, out
+aliasing v, strong decays that force shorter chunks, split/resume and
+determinism.
 """
 import numpy as np
 import pytest
@@ -60,6 +62,38 @@ def test_tiny_fp32():
 def test_shapes_k_ne_v(K, V):
     inp = wl.host_prefill_inputs([70, 130], 2, K, V, dtype="bf16", seed=K * 1000 + V)
     _check(inp)
+
+
+@pytest.mark.parametrize("K,V,dtype", [(30, 50, "bf16"), (33, 17, "f32"), (126, 130, "bf16")])
+def test_shapes_element_loads(K, V, dtype):
+    # odd K or V take the element-by-element loads; even sizes that are not a
+    # multiple of 4 take the vector loads with clamped tails
+    inp = wl.host_prefill_inputs([70, 130], 2, K, V, dtype=dtype, seed=K * 1000 + V + 7)
+    _check(inp)
+
+
+def test_unaligned_inputs_use_element_loads():
+    """q, k, v and g as views one element into larger buffers (2-byte or
+    4-byte aligned), which takes the element-by-element load path."""
+    import torch
+    import kda_recurrent_state_amd as kda
+    inp = wl.host_prefill_inputs([100, 64, 37], 2, 64, 64, dtype="bf16", seed=91)
+    print("case: unaligned q/k/v/g lengths=[100, 64, 37] H=2 K=V=64 bf16", flush=True)
+    d = device_inputs(inp)
+
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        view = buf[1:].view(t.shape)
+        view.copy_(t)
+        return view
+
+    o, f = kda.kda_chunk_prefill(shifted(d["q"]), shifted(d["k"]), shifted(d["v"]), shifted(d["g"]), d["beta"],
+                                 d["cu_seqlens"], initial_state=d["initial"])
+    torch.cuda.synchronize()
+    ro, rf = _ref(inp)
+    eo, ef = rel_l2(tensor_f64(o), ro), rel_l2(tensor_f64(f), rf)
+    print("  relL2 out %.3e final %.3e" % (eo, ef), flush=True)
+    assert eo <= REL_TOL and ef <= REL_TOL
 
 
 def test_bf16_ragged_varlen():
