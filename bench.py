@@ -28,11 +28,14 @@ sys.path.insert(0, ROOT)
 
 METRIC = "KDA prefill tokens/s (H=32,K=V=128) + state gather/scatter GB/s, 1 GPU"
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix peak of MI355X
 H, K, V = 32, 128, 128
 NUM_ROWS = 4096
 MAX_SELECTED = 256
 CHUNK_SRC = os.path.join(ROOT, "kda_recurrent_state_amd", "csrc", "chunk_prefill.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_prefill_e2e_traffic.json")
+SOURCES = [os.path.join(ROOT, "kda_recurrent_state_amd", "csrc", f)
+           for f in ("chunk_prefill.hip", "state_copy.hip", "decode.hip", "int8_ckpt.hip", "kda_api.cpp")]
 
 
 def chunk_bytes_per_launch(T: int, N: int) -> int:
@@ -44,6 +47,26 @@ def chunk_bytes_per_launch(T: int, N: int) -> int:
     """
     per_tok = 2 * K + 2 * K + 2 * V + 4 * K + 4 + 2 * V
     return T * H * per_tok + N * H * 2 * (K * V * 2) + 4 * (N + 1)
+
+
+def chunk_flops_per_token_head(C: int = 64, Kd: int = K, Vd: int = V) -> float:
+    """Algorithmic flops per token-head of the chunk form (multiply-add = 2),
+    counting only the triangles the method needs, for full chunks of C tokens
+    (stage order of page "PR #33465 完整报告", section "关键源码片段"):
+    A_kk (strict lower) and A_qk (lower) over K, the unit lower-triangular
+    inverse (C^3/3), W and U (lower-triangular times C x K and C x V),
+    V_new = U - W S, the state update Kbar^T V_new plus the decay, and
+    O = Qg S + A_qk V_new.  About 1.41e5 at C = 64, K = V = 128."""
+    lo, slo = C * (C + 1) / 2, C * (C - 1) / 2
+    per_chunk = (2 * slo * Kd + 2 * lo * Kd + C ** 3 / 3 + 2 * lo * Kd + 2 * lo * Vd + 2 * C * Kd * Vd
+                 + 2 * Kd * C * Vd + Kd * Vd + 2 * C * Kd * Vd + 2 * lo * Vd)
+    return per_chunk / C
+
+
+def pct(xs):
+    """p10 / p50 / p90 of a list of times."""
+    a = np.asarray(xs, dtype=np.float64)
+    return {"p10": float(np.percentile(a, 10)), "p50": float(np.percentile(a, 50)), "p90": float(np.percentile(a, 90))}
 
 
 def sha256_file(path: str) -> str:
@@ -386,7 +409,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this path runs on one GPU; --gpus %d is not supported (sequences and heads shard "
-              "across GPUs with no exchange, see DESIGN.md)" % args.gpus, file=sys.stderr)
+              "across GPUs with no exchange)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -456,6 +479,10 @@ def main():
     achieved = chunk_bytes / (c_avg * 1e-3) / 1e9
     traffic = stored_traffic(T, N)
     g_avg, s_avg = float(np.mean(g_ms)), float(np.mean(s_ms))
+    fl_tok = chunk_flops_per_token_head()
+    flops = fl_tok * T * H
+    t_hbm, t_mfma = chunk_bytes / (HBM_PEAK_GBPS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    t_roof = max(t_hbm, t_mfma)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -491,6 +518,14 @@ def main():
                       "scatter_frac_hbm": scatter_bytes / (s_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                       "gather_bytes": gather_bytes, "scatter_bytes": scatter_bytes},
         "chunk_tokens_per_s": T / (c_avg * 1e-3),
+        "mfma": {"flop_convention": "chunk form, triangles only, C=64 (%.0f flop per token-head)" % fl_tok,
+                 "algorithmic_tflops": flops / (c_avg * 1e-3) / 1e12,
+                 "frac_bf16_dense_peak": flops / (c_avg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+        "attainable": {"t_roof_ms": t_roof * 1e3, "t_meas_ms": c_avg,
+                       "frac": t_roof / (c_avg * 1e-3), "bound": "hbm" if t_hbm >= t_mfma else "mfma"},
+        "samples_ms": {"gather": g_ms, "chunk_prefill": c_ms, "scatter": s_ms},
+        "percentiles_ms": {"gather": pct(g_ms), "chunk_prefill": pct(c_ms), "scatter": pct(s_ms)},
+        "sources_sha256": {os.path.basename(f): sha256_file(f)[:16] for f in SOURCES},
         "gpu": torch.cuda.get_device_name(0),
     }
     print(json.dumps(line))

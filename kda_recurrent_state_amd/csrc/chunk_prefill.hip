@@ -21,10 +21,11 @@
 //   O        = scale (Q * 2^gamma) S + A_qk V_new
 //   S        = diag(2^gamma_L) S + Kbar^T V_new
 //
-// MI355X mapping (one workgroup of 4 wave64s per (sequence, head, V-block)):
+// MI355X mapping (one workgroup of BV/16 wave64s -- 4 or 8 -- per (sequence,
+// head, V-block of BV = 64 or 128 value columns)):
 //  * The workgroup walks its sequence chunk by chunk; the fp32 state block
 //    (K x BV) never leaves registers.  It is held in MFMA accumulator layout,
-//    wave w owning BV/4 value columns, and converted to bf16 B-operands for the
+//    wave w owning 16 value columns, and converted to bf16 B-operands for the
 //    W S and Q S products.  The serial chain (V_new, O, S update) touches no
 //    barrier: each wave works on its own columns with operands that the whole
 //    workgroup prepared in LDS.
