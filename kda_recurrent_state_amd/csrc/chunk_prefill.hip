@@ -316,7 +316,9 @@ __device__ __forceinline__ void store_state(const f32x4 (&S)[KT], void* dst, int
   }
 }
 
-template <int KP, int BV, bool kBF16>
+// kOut = false: maps of segments only (out == NULL); q, the query tiles, A_qk
+// and the output products are not computed.
+template <int KP, int BV, bool kBF16, bool kOut>
 __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
   using C = Cfg<KP, BV>;
   constexpr int NW = C::NW, NT = C::NT, RPW = C::RPW, CPL = C::CPL, VPL = C::VPL;
@@ -366,9 +368,11 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
   const int64_t srow = (n * H + h) * V;  // state row base of (n, h), in units of K elements
 
   // A_qk upper blocks are read by the output product but never written: zero once.
-  for (int e = tid; e < kC * kC; e += NT) {
-    const int r = e >> 6, c = e & 63;
-    if ((c >> 4) > (r >> 4)) sAqk[r * C::LDT + c] = (__bf16)0.f;
+  if constexpr (kOut) {
+    for (int e = tid; e < kC * kC; e += NT) {
+      const int r = e >> 6, c = e & 63;
+      if ((c >> 4) > (r >> 4)) sAqk[r * C::LDT + c] = (__bf16)0.f;
+    }
   }
 
   // ---- initial state, MFMA C layout: S[ct][e] = S(c = 16ct + 4lg + e, vcol) ----
@@ -751,26 +755,32 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
           const float e1 = __builtin_amdgcn_exp2f(d);   // 2^(gamma_i - gamma_m)
           const float e2 = __builtin_amdgcn_exp2f(-d);  // 2^(gamma_m - gamma_i)
           const float fkl = kx[r][cc] * e1 * bk;        // beta k^ 2^(gamma_i - gamma_m)
-          const float fql = qx[r][cc] * e1 * sq;        // scale q^ 2^(gamma_i - gamma_m)
           const float fkr = kx[r][cc] * e2 * rk[r];     // k^ 2^(gamma_m - gamma_i)
           kl[cc] = (__bf16)fkl;
-          ql[cc] = (__bf16)fql;
           kr[cc] = (__bf16)fkr;
-          qg[cc] = (__bf16)(fql * cg[cc]);              // scale q^ 2^gamma_i
+          if constexpr (kOut) {
+            const float fql = qx[r][cc] * e1 * sq;      // scale q^ 2^(gamma_i - gamma_m)
+            ql[cc] = (__bf16)fql;
+            qg[cc] = (__bf16)(fql * cg[cc]);            // scale q^ 2^gamma_i
+          }
           ke[cc][r] = (__bf16)(fkl * cg[cc]);           // beta k^ 2^gamma_i
           kb[cc][r] = (__bf16)(fkr * cb[cc]);           // k^ 2^(gamma_L - gamma_i)
         }
         if (CPL == 2) {
           typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
           *reinterpret_cast<bf16x2*>(sKL + i * C::LDK + c_lo) = bf16x2{kl[0], kl[CPL - 1]};
-          *reinterpret_cast<bf16x2*>(sQL + i * C::LDK + c_lo) = bf16x2{ql[0], ql[CPL - 1]};
           *reinterpret_cast<bf16x2*>(sKR + i * C::LDK + c_lo) = bf16x2{kr[0], kr[CPL - 1]};
-          *reinterpret_cast<bf16x2*>(sQg + i * C::LDKE + c_lo) = bf16x2{qg[0], qg[CPL - 1]};
+          if constexpr (kOut) {
+            *reinterpret_cast<bf16x2*>(sQL + i * C::LDK + c_lo) = bf16x2{ql[0], ql[CPL - 1]};
+            *reinterpret_cast<bf16x2*>(sQg + i * C::LDKE + c_lo) = bf16x2{qg[0], qg[CPL - 1]};
+          }
         } else {
           sKL[i * C::LDK + c_lo] = kl[0];
-          sQL[i * C::LDK + c_lo] = ql[0];
           sKR[i * C::LDK + c_lo] = kr[0];
-          sQg[i * C::LDKE + c_lo] = qg[0];
+          if constexpr (kOut) {
+            sQL[i * C::LDK + c_lo] = ql[0];
+            sQg[i * C::LDKE + c_lo] = qg[0];
+          }
         }
       }
       // transposed tiles: RPW consecutive rows of one channel, 16-byte stores
@@ -827,7 +837,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
             const int bj = pr - (bi * (bi + 1)) / 2;
             const bf16x8 rgt = ld8(sKR + (16 * bj + lr) * C::LDK + 32 * ks + 8 * lg);
             akk[m] = mfma(ld8(sKL + (16 * bi + lr) * C::LDK + 32 * ks + 8 * lg), rgt, akk[m]);
-            aqk[m] = mfma(ld8(sQL + (16 * bi + lr) * C::LDK + 32 * ks + 8 * lg), rgt, aqk[m]);
+            if constexpr (kOut) aqk[m] = mfma(ld8(sQL + (16 * bi + lr) * C::LDK + 32 * ks + 8 * lg), rgt, aqk[m]);
           }
         }
 #pragma unroll
@@ -840,7 +850,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int row = 16 * bi + 4 * lg + e;
-            sAqk[row * C::LDT + col] = (__bf16)(row >= col ? aqk[m][e] : 0.f);
+            if constexpr (kOut) sAqk[row * C::LDT + col] = (__bf16)(row >= col ? aqk[m][e] : 0.f);
             if (bi != bj) sAb[row * C::LDT + col] = (__bf16)(-akk[m][e]);
           }
           if (bi == bj) {  // rows 4lg..4lg+3 of column lr: one 16-byte store
@@ -971,21 +981,23 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     f32x4 O[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) O[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (kOut) {
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      bf16x8 a[4];
+      for (int ks = 0; ks < C::KS; ++ks) {
+        bf16x8 a[4];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) a[rt] = ld_perm(sQg + (16 * rt + lr) * C::LDKE + 32 * ks + 4 * lg);
+        for (int rt = 0; rt < 4; ++rt) a[rt] = ld_perm(sQg + (16 * rt + lr) * C::LDKE + 32 * ks + 4 * lg);
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) O[rt] = mfma(bS[ks], a[rt], O[rt]);
-    }
-#pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2)
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        if (32 * q2 > 16 * rt + 15) continue;
-        O[rt] = mfma(bV[q2], ld_perm(sAqk + (16 * rt + lr) * C::LDT + 32 * q2 + 4 * lg), O[rt]);
+        for (int rt = 0; rt < 4; ++rt) O[rt] = mfma(bS[ks], a[rt], O[rt]);
       }
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          if (32 * q2 > 16 * rt + 15) continue;
+          O[rt] = mfma(bV[q2], ld_perm(sAqk + (16 * rt + lr) * C::LDT + 32 * q2 + 4 * lg), O[rt]);
+        }
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ct = 0; ct < C::KT; ++ct) S[ct] *= *reinterpret_cast<const f32x4*>(sDec + 16 * ct + 4 * lg);
@@ -996,7 +1008,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
         S[ct] = mfma(ld_perm(sKB + (16 * ct + lr) * C::LDT + 32 * q2 + 4 * lg), bV[q2], S[ct]);
 
     // ---------------- output rows of this chunk ---------------------------
-    if (p.out == nullptr) {
+    if constexpr (!kOut) {
       // maps of a segment only (no outputs)
     } else if (kBF16 && p.ovec) {
       // stage through LDS (KR is dead), one 8-byte write per tile, and store
@@ -1189,10 +1201,18 @@ hipError_t launch_cfg(const Params& prm, bool bf16, hipStream_t stream) {
   const int64_t groups = (items + 7) / 8;
   const int64_t grid = groups * 8 * prm.nvb;
   constexpr int nt = Cfg<KP, BV>::NT;
-  if (bf16)
-    hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, true>), dim3((unsigned)grid), dim3(nt), 0, stream, prm);
-  else
-    hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, false>), dim3((unsigned)grid), dim3(nt), 0, stream, prm);
+  const dim3 g3((unsigned)grid), b3(nt);
+  if (prm.out) {
+    if (bf16)
+      hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, true, true>), g3, b3, 0, stream, prm);
+    else
+      hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, false, true>), g3, b3, 0, stream, prm);
+  } else {
+    if (bf16)
+      hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, true, false>), g3, b3, 0, stream, prm);
+    else
+      hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, false, false>), g3, b3, 0, stream, prm);
+  }
   return hipGetLastError();
 }
 
