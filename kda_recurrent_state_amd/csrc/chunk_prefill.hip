@@ -576,7 +576,10 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     // chunk length: the cap, the tokens left, and the next multiple of 64
     int L = (int)((len - t0) < (int64_t)Lcap ? (len - t0) : (int64_t)Lcap);
     L = L < kC - (int)(t0 & (kC - 1)) ? L : kC - (int)(t0 & (kC - 1));
-    lds_barrier();  // the previous chunk's LDS readers are done
+    // No barrier here: before phase 0's barrier this chunk writes only (beta
+    // V)^T and the gate totals, which the previous chunk read before its
+    // phase-E and phase-A barriers; every tile the previous chunk's phase E
+    // and output still read is rewritten only after phase 0's barrier.
     // Per-iteration copies of the lane indices, opaque to the optimiser: this
     // keeps every lane-dependent LDS address from being hoisted out of the
     // loop into a register of its own (which would force spills).
