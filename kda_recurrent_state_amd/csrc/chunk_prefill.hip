@@ -1127,72 +1127,119 @@ __global__ __launch_bounds__(1024) void seg_plan_kernel(const int32_t* __restric
 // S <- M S + b); 256 threads, K, V <= 128.  Writes each segment's initial
 // state S_in ([nmax, H, V, K] fp32) and the sequence's final state for these
 // columns.
+//
+// The map of a segment is stored as the state that pass 1b propagated from
+// the identity: row x of the [K][K] tile holds M's column x, so
+// S_new[r] = b[r] + sum_x T[x][r] S[x].  T is kept in LDS as stored (thread
+// r reads column r: consecutive addresses across lanes) and the next
+// segment's T and b are loaded into registers while this segment's product
+// runs (K % 4 == 0: 16-byte loads; other K: element loads, not prefetched).
 constexpr int kScanCols = 16;
+constexpr int kScanT = 256;                      // threads
+constexpr int kScanSL = kScanCols + 4;           // sS row stride (16-byte aligned rows)
+constexpr int kScanML = 128 + 4;                 // sT row stride
+constexpr int kScanV4 = 128 * 128 / 4 / kScanT;  // float4 of a 128 x 128 tile per thread
 
-__global__ __launch_bounds__(256) void seg_scan_kernel(const int32_t* __restrict__ sfirst, const float* __restrict__ bmap,
-                                                       const float* __restrict__ mmap, const void* __restrict__ init,
-                                                       int init_bf16, void* __restrict__ fin, int fin_bf16,
-                                                       float* __restrict__ sin, int64_t H, int64_t K, int64_t V) {
-  __shared__ float sS[128][kScanCols + 1];  // S[c][v - v0]
-  __shared__ float sM[128][129];            // M[c][c']
+__global__ __launch_bounds__(kScanT) void seg_scan_kernel(const int32_t* __restrict__ sfirst, const float* __restrict__ bmap,
+                                                          const float* __restrict__ mmap, const void* __restrict__ init,
+                                                          int init_bf16, void* __restrict__ fin, int fin_bf16,
+                                                          float* __restrict__ sin, int64_t H, int64_t K, int64_t V) {
+  __shared__ __attribute__((aligned(16))) float sS[128 * kScanSL];  // S[c][v - v0]
+  __shared__ __attribute__((aligned(16))) float sT[128 * kScanML];  // T[x][c]
   const int64_t ncb = (V + kScanCols - 1) / kScanCols;
   const int64_t item = blockIdx.x / ncb;
   const int64_t v0 = (blockIdx.x - item * ncb) * kScanCols;
   const int64_t n = item / H, h = item % H;
   const int tid = threadIdx.x;
   const int64_t srow = (n * H + h) * V;  // [.., H, V, K] row base of (n, h)
+  const bool vec = (K & 3) == 0;
+  const int nv4 = (int)(K * K / 4);      // float4 of a K x K tile
   // coalesced element order: e -> (column vl, channel c), c fastest
-  for (int e = tid; e < kScanCols * 128; e += 256) {
+  for (int e = tid; e < kScanCols * 128; e += kScanT) {
     const int c = e & 127, vl = e >> 7;
     float x = 0.f;
     if (init && c < K && v0 + vl < V) {
       const int64_t o = (srow + v0 + vl) * K + c;
       x = init_bf16 ? bf2f(static_cast<const unsigned short*>(init)[o]) : static_cast<const float*>(init)[o];
     }
-    sS[c][vl] = x;
+    sS[c * kScanSL + vl] = x;
   }
-  __syncthreads();
-  const int r = tid >> 1;                 // this thread's state row (key channel)
+  const int r = tid >> 1;                      // this thread's state row (key channel)
   const int j0 = (tid & 1) * (kScanCols / 2);  // and its 8 columns
-  for (int64_t sg = sfirst[n]; sg < sfirst[n + 1]; ++sg) {
-    const int64_t srow_s = (sg * H + h) * V;
-    const int64_t mrow_s = (sg * H + h) * K;
-    for (int e = tid; e < kScanCols * 128; e += 256) {
-      const int c = e & 127, vl = e >> 7;
-      if (v0 + vl < V && c < K) sin[(srow_s + v0 + vl) * K + c] = sS[c][vl];
+  const int64_t s0 = sfirst[n], s1 = sfirst[n + 1];
+  f32x4 tr[kScanV4];        // the next segment's T (vector path)
+  float br[kScanCols / 2];  // and this thread's b entries
+  auto fetch = [&](int64_t sg) {
+    const float* tb = mmap + (sg * H + h) * K * K;
+    if (vec) {
+#pragma unroll
+      for (int u = 0; u < kScanV4; ++u) {
+        const int f = u * kScanT + tid;
+        if (f < nv4) tr[u] = *reinterpret_cast<const f32x4*>(tb + 4 * (int64_t)f);
+      }
     }
-    for (int e = tid; e < 128 * 128; e += 256) {
-      const int c = e & 127, x = e >> 7;  // element (x, c) of the map tensor = M[c][x]
-      sM[c][x] = (c < K && x < K) ? mmap[(mrow_s + x) * K + c] : 0.f;
-    }
-    __syncthreads();
-    float acc[kScanCols / 2];
 #pragma unroll
     for (int j = 0; j < kScanCols / 2; ++j) {
       const int64_t v = v0 + j0 + j;
-      acc[j] = (r < K && v < V) ? bmap[(srow_s + v) * K + r] : 0.f;
+      br[j] = (r < K && v < V) ? bmap[((sg * H + h) * V + v) * K + r] : 0.f;
     }
-    if (r < K) {
-      for (int cp = 0; cp < K; ++cp) {
-        const float m = sM[r][cp];
+  };
+  if (s0 < s1) fetch(s0);
+  __syncthreads();
+  for (int64_t sg = s0; sg < s1; ++sg) {
+    const int64_t srow_s = (sg * H + h) * V;
+    for (int e = tid; e < kScanCols * 128; e += kScanT) {
+      const int c = e & 127, vl = e >> 7;
+      if (v0 + vl < V && c < K) sin[(srow_s + v0 + vl) * K + c] = sS[c * kScanSL + vl];
+    }
+    if (vec) {
+      const int q4 = (int)(K / 4);  // float4 per row
 #pragma unroll
-        for (int j = 0; j < kScanCols / 2; ++j) acc[j] += m * sS[cp][j0 + j];
+      for (int u = 0; u < kScanV4; ++u) {
+        const int f = u * kScanT + tid;
+        if (f < nv4) {
+          const int x = f / q4, c4 = f - x * q4;
+          *reinterpret_cast<f32x4*>(sT + x * kScanML + 4 * c4) = tr[u];
+        }
+      }
+    } else {
+      const float* tb = mmap + (sg * H + h) * K * K;
+      for (int e = tid; e < K * K; e += kScanT) {
+        const int x = (int)(e / K), c = (int)(e - x * K);
+        sT[x * kScanML + c] = tb[e];
+      }
+    }
+    float acc[kScanCols / 2];
+#pragma unroll
+    for (int j = 0; j < kScanCols / 2; ++j) acc[j] = br[j];
+    __syncthreads();
+    if (sg + 1 < s1) fetch(sg + 1);  // lands while the product below runs
+    if (r < K) {
+      for (int x = 0; x < K; ++x) {
+        const float m = sT[x * kScanML + r];
+        const f32x4 a = *reinterpret_cast<const f32x4*>(sS + x * kScanSL + j0);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(sS + x * kScanSL + j0 + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[j] += m * a[j];
+          acc[4 + j] += m * b[j];
+        }
       }
     }
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < kScanCols / 2; ++j) sS[r][j0 + j] = acc[j];
+    for (int j = 0; j < kScanCols / 2; ++j) sS[r * kScanSL + j0 + j] = acc[j];
     __syncthreads();
   }
   if (fin) {
-    for (int e = tid; e < kScanCols * 128; e += 256) {
+    for (int e = tid; e < kScanCols * 128; e += kScanT) {
       const int c = e & 127, vl = e >> 7;
       if (c < K && v0 + vl < V) {
         const int64_t o = (srow + v0 + vl) * K + c;
         if (fin_bf16)
-          static_cast<__bf16*>(fin)[o] = (__bf16)sS[c][vl];
+          static_cast<__bf16*>(fin)[o] = (__bf16)sS[c * kScanSL + vl];
         else
-          static_cast<float*>(fin)[o] = sS[c][vl];
+          static_cast<float*>(fin)[o] = sS[c * kScanSL + vl];
       }
     }
   }
