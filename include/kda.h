@@ -64,7 +64,7 @@ typedef enum {
   KDA_E_OVERLAP = 5,     /* cache row stride smaller than the row payload (pages overlap) */
   KDA_E_UNSUPPORTED = 6, /* a size this build has no kernel for (e.g. K > 128)            */
   KDA_E_WORKSPACE = 7,   /* workspace missing or smaller than kda_chunk_prefill_workspace_size */
-  KDA_E_ALIAS = 8,       /* output partially overlaps an input                          */
+  KDA_E_ALIAS = 8,       /* an output overlaps an input or another output               */
   KDA_E_HIP = 9          /* the HIP runtime reported an error                           */
 } kda_status_t;
 
@@ -141,15 +141,21 @@ kda_status_t kda_state_scatter(const kda_state_cache_t* cache, const void* indic
  *  initial_state   -- [N, H, V, K] in initial_dtype, element (n,h,v,c) =
  *                     S[c][v]; or NULL for zero initial states.
  *  out             -- [T, H, V] in qkv_dtype.  It may be exactly v (the
- *                     output then overwrites v, [P3]); any other overlap
- *                     with an input is an error.
+ *                     output then overwrites v, [P3]).
  *  final_state     -- [N, H, V, K] in final_dtype, or NULL.  fp32 states are
  *                     rounded to bf16 to nearest even when final_dtype is bf16.
+ *                     It may be exactly initial_state with the same dtype
+ *                     (the states are then updated in place).
  *  scale           -- read-out scale ([P3] uses K^-1/2).
  *  use_qk_l2norm   -- nonzero: q and k rows are divided by sqrt(|x|^2 + 1e-6).
  *  workspace       -- device scratch of at least
  *                     kda_chunk_prefill_workspace_size(T, N, H, K, V) bytes
  *                     (may be NULL when that size is 0).
+ * Aliasing (checked on the host, KDA_E_ALIAS): the outputs -- out,
+ * final_state, ckpt_states and the workspace's first
+ * kda_chunk_prefill_workspace_size bytes -- overlap neither each other nor
+ * any input (q, k, v, g, beta, cu_seqlens, initial_state, ckpt_cu), except
+ * for the two exact aliases above.
  * Per sequence n and head h, with S the K x V fp32 state, this computes for
  * each token t in order ([P2] section 1.1 and the gated delta rule):
  *   S <- (I - beta_t k_t k_t^T) Diag(exp g_t) S + beta_t k_t v_t^T
@@ -192,7 +198,7 @@ typedef struct {
    *  ckpt_cu       -- [N+1] int32 device array of checkpoint row offsets,
    *                   non-decreasing (not checked).
    *  ckpt_states   -- device output, num_ckpt rows, or NULL for none.  It must
-   *                   not overlap any other argument (not checked). */
+   *                   not overlap any other argument (checked, KDA_E_ALIAS). */
   int64_t ckpt_interval;
   const int32_t* ckpt_cu;
   void* ckpt_states;
@@ -253,8 +259,10 @@ typedef struct {
  * computed in fp32.  An index outside [0, num_rows) marks a padding slot: its
  * output is zero and no cache row is read or written.
  * Preconditions (not checked, no device-to-host scan): valid indices are
- * unique within one call (rows are updated concurrently).  out must not
- * overlap the cache (checked against the cache's address span).
+ * unique within one call (rows are updated concurrently).  Aliasing (checked
+ * on the host, KDA_E_ALIAS): neither the cache's address span nor out
+ * overlaps q, k, v, g, beta, state_indices or the other, except that out may
+ * be exactly v.
  * N == 0 validates the cache view and enqueues nothing.
  * Errors: KDA_E_NULL, KDA_E_DTYPE, KDA_E_SHAPE, KDA_E_LAYOUT, KDA_E_OVERLAP,
  * KDA_E_UNSUPPORTED, KDA_E_ALIAS, KDA_E_HIP.
@@ -288,9 +296,11 @@ typedef struct {
  *             ties to even), code = 0 where scale_c == 0.
  * Other entries are skipped.  packed: [num_selected, H, V, K] in packed_dtype
  * (fp32 or bf16), contiguous.  Preconditions (not checked): valid slots are
- * unique; finite inputs.  num_selected == 0 enqueues nothing.
+ * unique; finite inputs.  The store's qdata and scale ranges must not overlap
+ * packed or indices (checked, KDA_E_ALIAS).  num_selected == 0 enqueues
+ * nothing.
  * Errors: KDA_E_NULL, KDA_E_DTYPE, KDA_E_SHAPE, KDA_E_OVERLAP, KDA_E_UNSUPPORTED,
- * KDA_E_HIP.
+ * KDA_E_ALIAS, KDA_E_HIP.
  */
 kda_status_t kda_ckpt_quantize_scatter(const kda_int8_store_t* store, const void* indices, kda_index_t index_type,
                                        int64_t num_selected, const void* packed, kda_dtype_t packed_dtype,
@@ -302,7 +312,8 @@ kda_status_t kda_ckpt_quantize_scatter(const kda_int8_store_t* store, const void
  *       if 0 <= indices[i] < num_slots and (flags == NULL or flags[i] != 0),
  *   packed[i] = zeros otherwise.
  * Every row of packed is written; the result can seed kda_chunk_prefill's
- * initial_state or go to active cache rows through kda_state_scatter.
+ * initial_state or go to active cache rows through kda_state_scatter.  packed
+ * must not overlap the store, indices or flags (checked, KDA_E_ALIAS).
  * Errors as for kda_ckpt_quantize_scatter.
  */
 kda_status_t kda_ckpt_dequantize_gather(const kda_int8_store_t* store, const void* indices, kda_index_t index_type,

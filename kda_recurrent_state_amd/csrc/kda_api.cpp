@@ -77,6 +77,32 @@ bool ranges_overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes
   return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
 }
 
+// A device byte range; an absent argument has p == NULL or bytes == 0.
+struct Span {
+  const void* p;
+  int64_t bytes;
+};
+
+bool spans_overlap(const Span& a, const Span& b) {
+  return a.p && b.p && a.bytes > 0 && b.bytes > 0 && ranges_overlap(a.p, a.bytes, b.p, b.bytes);
+}
+
+// Every output must be disjoint from every input and from the other outputs,
+// except for the pairs (outs[i], ins[same[i]]) that are the very same range
+// (same[i] < 0: no such exception).
+bool alias_error(const Span* outs, const int* same, int nouts, const Span* ins, int nins) {
+  for (int i = 0; i < nouts; ++i) {
+    for (int j = 0; j < nins; ++j) {
+      if (!spans_overlap(outs[i], ins[j])) continue;
+      if (same[i] == j && outs[i].p == ins[j].p && outs[i].bytes == ins[j].bytes) continue;
+      return true;
+    }
+    for (int j = i + 1; j < nouts; ++j)
+      if (spans_overlap(outs[i], outs[j])) return true;
+  }
+  return false;
+}
+
 kda_status_t int8_common(bool quantize, const kda_int8_store_t* st, const void* indices, kda_index_t it,
                          int64_t num_selected, const uint8_t* flags, void* packed, kda_dtype_t pdt, void* stream) {
   if (!st) return KDA_E_NULL;
@@ -94,8 +120,24 @@ kda_status_t int8_common(bool quantize, const kda_int8_store_t* st, const void* 
   if (!valid_dtype(pdt)) return KDA_E_DTYPE;
   if (it != KDA_I32 && it != KDA_I64) return KDA_E_DTYPE;
   if (num_selected < 0) return KDA_E_SHAPE;
+  if (num_selected > ((int64_t)1 << 40) / qpay) return KDA_E_SHAPE;
   if (num_selected == 0) return KDA_OK;
   if (!indices || !packed) return KDA_E_NULL;
+  {
+    const Span qd{st->qdata, (st->num_slots - 1) * st->qdata_stride0 + qpay};
+    const Span sc{st->scale, ((st->num_slots - 1) * st->scale_stride0 + spay) * 4};
+    const Span pk{packed, num_selected * qpay * dtype_bytes(pdt)};
+    const Span ix{indices, num_selected * (it == KDA_I64 ? 8 : 4)};
+    const Span fl{quantize ? nullptr : flags, num_selected};
+    const int none[2] = {-1, -1};
+    if (quantize) {
+      const Span outs[2] = {qd, sc}, ins[2] = {pk, ix};
+      if (alias_error(outs, none, 2, ins, 2)) return KDA_E_ALIAS;
+    } else {
+      const Span outs[1] = {pk}, ins[4] = {qd, sc, ix, fl};
+      if (alias_error(outs, none, 1, ins, 4)) return KDA_E_ALIAS;
+    }
+  }
   hipError_t e = kda::launch_int8_ckpt(quantize, *st, indices, it == KDA_I64, num_selected, quantize ? nullptr : flags,
                                        packed, pdt == KDA_BF16, static_cast<hipStream_t>(stream));
   return hip_status(quantize ? "kda_ckpt_quantize_scatter launch" : "kda_ckpt_dequantize_gather launch", e);
@@ -134,23 +176,34 @@ kda_status_t kda_chunk_prefill(const kda_prefill_args_t* a, void* stream) {
     if (!valid_dtype(a->ckpt_dtype)) return KDA_E_DTYPE;
   }
   if (a->T > ((int64_t)1 << 40) / (a->H * (a->K > a->V ? a->K : a->V))) return KDA_E_SHAPE;
+  if (a->N > ((int64_t)1 << 40) / (a->H * a->V * a->K)) return KDA_E_SHAPE;
+  if (a->ckpt_states && a->num_ckpt > ((int64_t)1 << 40) / (a->H * a->V * a->K)) return KDA_E_SHAPE;
   if (a->N == 0) return KDA_OK;
   if (!a->cu_seqlens) return KDA_E_NULL;
   if (a->T > 0 && (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->out)) return KDA_E_NULL;
   const size_t need = kda::chunk_prefill_workspace_bytes(a->T, a->N, a->H, a->K, a->V);
-  if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return KDA_E_WORKSPACE;
-  const int64_t eb = dtype_bytes(a->qkv_dtype);
-  if (a->T > 0) {
-    const int64_t ob = a->T * a->H * a->V * eb;
-    const int64_t kb = a->T * a->H * a->K * eb;
-    if (a->out != a->v && ranges_overlap(a->out, ob, a->v, ob)) return KDA_E_ALIAS;
-    if (ranges_overlap(a->out, ob, a->q, kb) || ranges_overlap(a->out, ob, a->k, kb) ||
-        ranges_overlap(a->out, ob, a->g, a->T * a->H * a->K * 4))
-      return KDA_E_ALIAS;
-    if (a->final_state &&
-        ranges_overlap(a->out, ob, a->final_state, a->N * a->H * a->V * a->K * dtype_bytes(a->final_dtype)))
-      return KDA_E_ALIAS;
+  {
+    // out may be exactly v and final_state exactly initial_state (same
+    // dtype); any other overlap between an output and an argument is an error
+    const int64_t eb = dtype_bytes(a->qkv_dtype), TH = a->T * a->H, NHVK = a->N * a->H * a->V * a->K;
+    const Span vin{a->v, TH * a->V * eb};
+    const Span init{a->initial_state, a->initial_state ? NHVK * dtype_bytes(a->initial_dtype) : 0};
+    const Span ins[8] = {{a->q, TH * a->K * eb},
+                         {a->k, TH * a->K * eb},
+                         vin,
+                         {a->g, TH * a->K * 4},
+                         {a->beta, TH * dtype_bytes(a->beta_dtype)},
+                         {a->cu_seqlens, (a->N + 1) * 4},
+                         init,
+                         {a->ckpt_states ? a->ckpt_cu : nullptr, (a->N + 1) * 4}};
+    const Span outs[4] = {{a->out, TH * a->V * eb},
+                          {a->final_state, a->final_state ? NHVK * dtype_bytes(a->final_dtype) : 0},
+                          {a->ckpt_states, a->ckpt_states ? a->num_ckpt * a->H * a->V * a->K * dtype_bytes(a->ckpt_dtype) : 0},
+                          {need > 0 ? a->workspace : nullptr, (int64_t)need}};
+    const int same[4] = {2, 6, -1, -1};
+    if (alias_error(outs, same, 4, ins, 8)) return KDA_E_ALIAS;
   }
+  if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return KDA_E_WORKSPACE;
   hipError_t e = kda::launch_chunk_prefill(*a, static_cast<hipStream_t>(stream));
   return hip_status("kda_chunk_prefill launch", e);
 }
@@ -169,15 +222,21 @@ kda_status_t kda_recurrent_decode(const kda_state_cache_t* cache, const kda_deco
   if (a->N > ((int64_t)1 << 40) / (a->H * (a->K > a->V ? a->K : a->V))) return KDA_E_SHAPE;
   if (a->N == 0) return KDA_OK;
   if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->state_indices || !a->out) return KDA_E_NULL;
-  const int64_t eb = dtype_bytes(a->qkv_dtype);
-  const int64_t ob = a->N * a->H * a->V * eb;
-  const int64_t kb = a->N * a->H * a->K * eb;
-  if (a->out != a->v && ranges_overlap(a->out, ob, a->v, ob)) return KDA_E_ALIAS;
-  if (ranges_overlap(a->out, ob, a->q, kb) || ranges_overlap(a->out, ob, a->k, kb) ||
-      ranges_overlap(a->out, ob, a->g, a->N * a->H * a->K * 4))
-    return KDA_E_ALIAS;
-  const int64_t span = ((cache->num_rows - 1) * cache->stride[0] + payload) * dtype_bytes(cache->dtype);
-  if (ranges_overlap(a->out, ob, cache->data, span)) return KDA_E_ALIAS;
+  {
+    // the cache rows are updated in place; out may be exactly v; any other
+    // overlap between the cache or out and an argument is an error
+    const int64_t eb = dtype_bytes(a->qkv_dtype), NH = a->N * a->H;
+    const Span ins[6] = {{a->q, NH * a->K * eb},
+                         {a->k, NH * a->K * eb},
+                         {a->v, NH * a->V * eb},
+                         {a->g, NH * a->K * 4},
+                         {a->beta, NH * dtype_bytes(a->beta_dtype)},
+                         {a->state_indices, a->N * (a->index_type == KDA_I64 ? 8 : 4)}};
+    const Span outs[2] = {{a->out, NH * a->V * eb},
+                          {cache->data, ((cache->num_rows - 1) * cache->stride[0] + payload) * dtype_bytes(cache->dtype)}};
+    const int same[2] = {2, -1};
+    if (alias_error(outs, same, 2, ins, 6)) return KDA_E_ALIAS;
+  }
   hipError_t e = kda::launch_recurrent_decode(*cache, *a, static_cast<hipStream_t>(stream));
   return hip_status("kda_recurrent_decode launch", e);
 }
@@ -205,7 +264,7 @@ const char* kda_status_string(kda_status_t s) {
     case KDA_E_OVERLAP: return "KDA_E_OVERLAP: cache row stride is smaller than the row payload";
     case KDA_E_UNSUPPORTED: return "KDA_E_UNSUPPORTED: no kernel for these sizes";
     case KDA_E_WORKSPACE: return "KDA_E_WORKSPACE: workspace missing or too small";
-    case KDA_E_ALIAS: return "KDA_E_ALIAS: output overlaps an input";
+    case KDA_E_ALIAS: return "KDA_E_ALIAS: an output overlaps an input or another output";
     case KDA_E_HIP: return "KDA_E_HIP: HIP runtime error";
   }
   return "unknown kda_status_t";

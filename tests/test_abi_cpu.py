@@ -134,6 +134,34 @@ def test_prefill_rejections(lib, kw, status):
     assert lib.kda_chunk_prefill(ctypes.byref(a), None) == status
 
 
+@pytest.mark.parametrize("kw", [
+    dict(out=0x5000 + 40),                                    # out over beta
+    dict(out=0x7000 - 100),                                   # out over cu_seqlens
+    dict(initial_state=0x6000 + 64),                          # initial state under out
+    dict(final_state=0x1000),                                 # final state over q
+    dict(final_state=0x8000, initial_state=0x8000, final_dtype=1),      # same address, other dtype
+    dict(final_state=0x8000 + 4, initial_state=0x8000),       # partial overlap
+    dict(ckpt_states=0x2000, ckpt_cu=0xa000, ckpt_interval=64, num_ckpt=1),   # checkpoints over k
+    dict(ckpt_states=0x9000, ckpt_cu=0x6000, ckpt_interval=64, num_ckpt=1),   # ckpt_cu under out
+    dict(ckpt_states=0x9000, ckpt_cu=0xa000, ckpt_interval=64, num_ckpt=1, final_state=0x9000 + 8),  # two outputs
+    dict(N=2, workspace=0x3000, workspace_bytes=1 << 20),     # workspace over v
+])
+def test_prefill_alias_rejections(lib, kw):
+    a = _args(**kw)
+    assert lib.kda_chunk_prefill(ctypes.byref(a), None) == 8
+
+
+@pytest.mark.parametrize("kw", [
+    dict(N=2, out=0x3000),                                    # out is exactly v
+    dict(N=2, final_state=0x8000, initial_state=0x8000),      # states updated in place
+])
+def test_prefill_exact_aliases_pass_validation(lib, kw):
+    # N = 2 needs a workspace, which is checked after aliasing: the call stops
+    # there, before any launch
+    a = _args(**kw)
+    assert lib.kda_chunk_prefill(ctypes.byref(a), None) == 7
+
+
 def test_prefill_empty_batch_is_ok(lib):
     a = _args(N=0, T=0)
     assert lib.kda_chunk_prefill(ctypes.byref(a), None) == 0
@@ -171,6 +199,18 @@ def test_decode_rejections(lib, ckw, akw, status):
     assert lib.kda_recurrent_decode(ctypes.byref(d), ctypes.byref(a), None) == status
 
 
+@pytest.mark.parametrize("akw", [
+    dict(out=0x500000 + 4),                   # out over beta
+    dict(out=0x700000),                       # out over state_indices
+    dict(q=0x1000 + 4),                       # q inside the cache span (updated in place)
+    dict(state_indices=0x1000),               # indices inside the cache span
+])
+def test_decode_alias_rejections(lib, akw):
+    d = _cache()
+    a = _dargs(**akw)
+    assert lib.kda_recurrent_decode(ctypes.byref(d), ctypes.byref(a), None) == 8
+
+
 def test_decode_empty_batch_is_ok(lib):
     d = _cache()
     a = _dargs(N=0, q=0, k=0, v=0, g=0, beta=0, out=0, state_indices=0)
@@ -202,6 +242,17 @@ def test_int8_store_rejections(lib, kw, status):
     d = _store(**kw)
     assert lib.kda_ckpt_quantize_scatter(ctypes.byref(d), 0x1000, 0, 2, 0x2000, 0, None) == status
     assert lib.kda_ckpt_dequantize_gather(ctypes.byref(d), 0x1000, 0, 2, None, 0x2000, 0, None) == status
+
+
+def test_int8_alias_rejections(lib):
+    d = _store()
+    # quantize writes the store: packed and indices must stay outside it
+    assert lib.kda_ckpt_quantize_scatter(ctypes.byref(d), 0x1000, 0, 2, 0x100000 + 8, 0, None) == 8
+    assert lib.kda_ckpt_quantize_scatter(ctypes.byref(d), 0x900000, 0, 2, 0x2000, 0, None) == 8
+    # dequantize writes packed: the store, indices and flags must stay outside it
+    assert lib.kda_ckpt_dequantize_gather(ctypes.byref(d), 0x1000, 0, 2, None, 0x900000 - 16, 0, None) == 8
+    assert lib.kda_ckpt_dequantize_gather(ctypes.byref(d), 0x1000, 0, 2, 0x2000, 0x2000, 0, None) == 8
+    assert lib.kda_ckpt_dequantize_gather(ctypes.byref(d), 0x2000 + 64, 0, 2, None, 0x2000, 0, None) == 8
 
 
 def test_int8_selection_arguments(lib):

@@ -4,8 +4,8 @@ Small cases are compared over every element; they span several chunks and
 tiles, ragged tails, K != V, V-split blocks, zero-length sequences, fp32 and
 bf16 I/O, vector and element-by-element loads (odd K or V, sizes that are not
 a multiple of 4, unaligned tensors), no initial state, bf16 final states, out
-aliasing v, strong decays that force shorter chunks, split/resume and
-determinism.
+aliasing v, final states written in place over the initial states, strong
+decays that force shorter chunks, split/resume and determinism.
 """
 import numpy as np
 import pytest
@@ -92,6 +92,29 @@ def test_unaligned_inputs_use_element_loads():
     torch.cuda.synchronize()
     ro, rf = _ref(inp)
     eo, ef = rel_l2(tensor_f64(o), ro), rel_l2(tensor_f64(f), rf)
+    print("  relL2 out %.3e final %.3e" % (eo, ef), flush=True)
+    assert eo <= REL_TOL and ef <= REL_TOL
+
+
+@pytest.mark.parametrize("lengths,H,K,V,init_dtype", [
+    ([300, 64, 129, 0], 2, 128, 128, "f32"),
+    ([17000], 2, 64, 64, "bf16"),             # segment-parallel path
+])
+def test_final_state_in_place(lengths, H, K, V, init_dtype):
+    """final_state is initial_state: every (sequence, head) state is read
+    before it is overwritten, so the update may run in place."""
+    import torch
+    import kda_recurrent_state_amd as kda
+    inp = wl.host_prefill_inputs(lengths, H, K, V, dtype="bf16", seed=sum(lengths) + 3, init_dtype=init_dtype)
+    print("case: in-place states lengths=%s H=%d K=%d V=%d init=%s" % (lengths, H, K, V, init_dtype), flush=True)
+    d = device_inputs(inp)
+    st = d["initial"].clone()
+    o, f = kda.kda_chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], initial_state=st,
+                                 final_state=st)
+    torch.cuda.synchronize()
+    assert f.data_ptr() == st.data_ptr()
+    ro, rf = _ref(inp)
+    eo, ef = rel_l2(tensor_f64(o), ro), rel_l2(tensor_f64(st), rf)
     print("  relL2 out %.3e final %.3e" % (eo, ef), flush=True)
     assert eo <= REL_TOL and ef <= REL_TOL
 
