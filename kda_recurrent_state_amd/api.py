@@ -24,16 +24,26 @@ def _dtype_code(t: torch.Tensor, what: str) -> int:
     return _DT[t.dtype]
 
 
-def _stream_handle(stream) -> int:
+def _stream_handle(stream, device) -> int:
+    """The given stream, or the current stream of ``device``."""
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(device)
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _require_cuda(*ts):
+def _device(*ts) -> torch.device:
+    """The one device that all given tensors live on (device tensors only)."""
+    dev = None
     for t in ts:
-        if t is not None and not t.is_cuda:
+        if t is None:
+            continue
+        if not t.is_cuda:
             raise ValueError("libkda works on device tensors; got a %s tensor" % t.device)
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("libkda arguments must share one device; got %s and %s" % (dev, t.device))
+    return dev
 
 
 def cache_descriptor(cache: torch.Tensor) -> StateCache:
@@ -61,7 +71,7 @@ def kda_state_gather(cache: torch.Tensor, indices: torch.Tensor, flags: Optional
                      packed: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """packed[i] = cache[indices[i]] if valid and flagged, else zeros (all rows written)."""
     lib = _lib.load_library()
-    _require_cuda(cache, indices, flags, packed)
+    dev = _device(cache, indices, flags, packed)
     if indices.dim() != 1 or not indices.is_contiguous():
         raise KDAError("kda_state_gather", 3, "indices must be a contiguous 1-D tensor")
     S = indices.shape[0]
@@ -75,8 +85,9 @@ def kda_state_gather(cache: torch.Tensor, indices: torch.Tensor, flags: Optional
             raise KDAError("kda_state_gather", 2, "flags must be a contiguous bool/uint8 tensor of length S")
         fptr = flags.data_ptr()
     d = cache_descriptor(cache)
-    st = lib.kda_state_gather(ctypes.byref(d), indices.data_ptr(), _index_code(indices), S, fptr,
-                              packed.data_ptr(), _stream_handle(stream))
+    with torch.cuda.device(dev):
+        st = lib.kda_state_gather(ctypes.byref(d), indices.data_ptr(), _index_code(indices), S, fptr,
+                                  packed.data_ptr(), _stream_handle(stream, dev))
     _lib.check("kda_state_gather", st)
     return packed
 
@@ -84,15 +95,16 @@ def kda_state_gather(cache: torch.Tensor, indices: torch.Tensor, flags: Optional
 def kda_state_scatter(cache: torch.Tensor, indices: torch.Tensor, packed: torch.Tensor, stream=None) -> None:
     """cache[indices[i]] = packed[i] for every valid index (flags play no part)."""
     lib = _lib.load_library()
-    _require_cuda(cache, indices, packed)
+    dev = _device(cache, indices, packed)
     if indices.dim() != 1 or not indices.is_contiguous():
         raise KDAError("kda_state_scatter", 3, "indices must be a contiguous 1-D tensor")
     S = indices.shape[0]
     if packed.dtype != cache.dtype or not packed.is_contiguous() or tuple(packed.shape) != (S,) + tuple(cache.shape[1:]):
         raise KDAError("kda_state_scatter", 3, "packed must be a contiguous [S,H,V,K] tensor of the cache dtype")
     d = cache_descriptor(cache)
-    st = lib.kda_state_scatter(ctypes.byref(d), indices.data_ptr(), _index_code(indices), S, packed.data_ptr(),
-                               _stream_handle(stream))
+    with torch.cuda.device(dev):
+        st = lib.kda_state_scatter(ctypes.byref(d), indices.data_ptr(), _index_code(indices), S, packed.data_ptr(),
+                                   _stream_handle(stream, dev))
     _lib.check("kda_state_scatter", st)
 
 
@@ -120,7 +132,7 @@ def kda_chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torc
     (j+1)*ckpt_interval tokens; ckpt_interval is a positive multiple of 64.
     """
     lib = _lib.load_library()
-    _require_cuda(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, workspace, ckpt_cu, ckpt_states)
+    dev = _device(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, workspace, ckpt_cu, ckpt_states)
     if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
         raise KDAError("kda_chunk_prefill", 3, "q,k must be [T,H,K] and v [T,H,V]")
     T, H, K = (int(x) for x in q.shape)
@@ -135,7 +147,7 @@ def kda_chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torc
         raise KDAError("kda_chunk_prefill", 2, "g must be float32 [T,H,K]")
     if tuple(beta.shape) != (T, H):
         raise KDAError("kda_chunk_prefill", 3, "beta must be [T,H]")
-    if cu_seqlens.dtype != torch.int32 or N < 0:
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or N < 0:
         raise KDAError("kda_chunk_prefill", 2, "cu_seqlens must be int32 [N+1]")
     if out is None:
         out = torch.empty((T, H, V), dtype=q.dtype, device=q.device)
@@ -177,7 +189,8 @@ def kda_chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torc
         a.ckpt_states = ckpt_states.data_ptr()
         a.num_ckpt = int(ckpt_states.shape[0])
         a.ckpt_dtype = _dtype_code(ckpt_states, "kda_chunk_prefill")
-    st = lib.kda_chunk_prefill(ctypes.byref(a), _stream_handle(stream))
+    with torch.cuda.device(dev):
+        st = lib.kda_chunk_prefill(ctypes.byref(a), _stream_handle(stream, dev))
     _lib.check("kda_chunk_prefill", st)
     return out, final_state
 
@@ -193,7 +206,7 @@ def kda_recurrent_decode(cache: torch.Tensor, state_indices: torch.Tensor, q: to
     (may be ``v``).  Valid indices must be unique.
     """
     lib = _lib.load_library()
-    _require_cuda(cache, state_indices, q, k, v, g, beta, out)
+    dev = _device(cache, state_indices, q, k, v, g, beta, out)
     if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
         raise KDAError("kda_recurrent_decode", 3, "q,k must be [N,H,K] and v [N,H,V]")
     N, H, K = (int(x) for x in q.shape)
@@ -226,7 +239,8 @@ def kda_recurrent_decode(cache: torch.Tensor, state_indices: torch.Tensor, q: to
     a.out = out.data_ptr()
     a.scale = float(K ** -0.5 if scale is None else scale)
     a.use_qk_l2norm = 1 if use_qk_l2norm else 0
-    st = lib.kda_recurrent_decode(ctypes.byref(d), ctypes.byref(a), _stream_handle(stream))
+    with torch.cuda.device(dev):
+        st = lib.kda_recurrent_decode(ctypes.byref(d), ctypes.byref(a), _stream_handle(stream, dev))
     _lib.check("kda_recurrent_decode", st)
     return out
 
@@ -253,16 +267,17 @@ def kda_ckpt_quantize_scatter(qdata: torch.Tensor, scale: torch.Tensor, indices:
                               stream=None) -> None:
     """Slots indices[i] of the INT8 store <- quantised packed[i] (invalid slots skipped)."""
     lib = _lib.load_library()
-    _require_cuda(qdata, scale, indices, packed)
+    dev = _device(qdata, scale, indices, packed)
     if indices.dim() != 1 or not indices.is_contiguous():
         raise KDAError("kda_ckpt_quantize_scatter", 3, "indices must be a contiguous 1-D tensor")
     S = int(indices.shape[0])
     if tuple(packed.shape) != (S,) + tuple(qdata.shape[1:]) or not packed.is_contiguous():
         raise KDAError("kda_ckpt_quantize_scatter", 3, "packed must be a contiguous [S,H,V,K] tensor")
     d = int8_store_descriptor(qdata, scale)
-    st = lib.kda_ckpt_quantize_scatter(ctypes.byref(d), indices.data_ptr(), _index_code(indices), S,
-                                       packed.data_ptr(), _dtype_code(packed, "kda_ckpt_quantize_scatter"),
-                                       _stream_handle(stream))
+    with torch.cuda.device(dev):
+        st = lib.kda_ckpt_quantize_scatter(ctypes.byref(d), indices.data_ptr(), _index_code(indices), S,
+                                           packed.data_ptr(), _dtype_code(packed, "kda_ckpt_quantize_scatter"),
+                                           _stream_handle(stream, dev))
     _lib.check("kda_ckpt_quantize_scatter", st)
 
 
@@ -271,7 +286,7 @@ def kda_ckpt_dequantize_gather(qdata: torch.Tensor, scale: torch.Tensor, indices
                                dtype: torch.dtype = torch.float32, stream=None) -> torch.Tensor:
     """packed[i] = dequantised slot indices[i] if valid and flagged, else zeros."""
     lib = _lib.load_library()
-    _require_cuda(qdata, scale, indices, flags, packed)
+    dev = _device(qdata, scale, indices, flags, packed)
     if indices.dim() != 1 or not indices.is_contiguous():
         raise KDAError("kda_ckpt_dequantize_gather", 3, "indices must be a contiguous 1-D tensor")
     S = int(indices.shape[0])
@@ -285,9 +300,10 @@ def kda_ckpt_dequantize_gather(qdata: torch.Tensor, scale: torch.Tensor, indices
             raise KDAError("kda_ckpt_dequantize_gather", 2, "flags must be a contiguous bool/uint8 tensor of length S")
         fptr = flags.data_ptr()
     d = int8_store_descriptor(qdata, scale)
-    st = lib.kda_ckpt_dequantize_gather(ctypes.byref(d), indices.data_ptr(), _index_code(indices), S, fptr,
-                                        packed.data_ptr(), _dtype_code(packed, "kda_ckpt_dequantize_gather"),
-                                        _stream_handle(stream))
+    with torch.cuda.device(dev):
+        st = lib.kda_ckpt_dequantize_gather(ctypes.byref(d), indices.data_ptr(), _index_code(indices), S, fptr,
+                                            packed.data_ptr(), _dtype_code(packed, "kda_ckpt_dequantize_gather"),
+                                            _stream_handle(stream, dev))
     _lib.check("kda_ckpt_dequantize_gather", st)
     return packed
 

@@ -286,6 +286,22 @@ def test_status_strings(lib):
     assert b"KDA_OK" in lib.kda_status_string(0)
 
 
+def test_binding_resolves_one_device():
+    """Every call runs on the device its tensors share; host tensors and
+    tensors on several devices are refused before anything is launched."""
+    import types
+    import torch
+    from kda_recurrent_state_amd import api
+    d0, d1 = torch.device("cuda", 0), torch.device("cuda", 1)
+    t0 = types.SimpleNamespace(is_cuda=True, device=d0)
+    t1 = types.SimpleNamespace(is_cuda=True, device=d1)
+    assert api._device(t0, None, t0) == d0
+    with pytest.raises(ValueError, match="one device"):
+        api._device(t0, t1)
+    with pytest.raises(ValueError, match="device tensors"):
+        api._device(t0, torch.zeros(1))
+
+
 def test_binding_refuses_without_library(tmp_path):
     from kda_recurrent_state_amd import _lib
     saved = _lib._lib
