@@ -62,7 +62,7 @@ typedef enum {
   KDA_E_SHAPE = 3,       /* negative or zero size where a positive one is required       */
   KDA_E_LAYOUT = 4,      /* cache inner dims [H,V,K] are not dense                       */
   KDA_E_OVERLAP = 5,     /* cache row stride smaller than the row payload (pages overlap) */
-  KDA_E_UNSUPPORTED = 6, /* a size this build has no kernel for (e.g. K > 128)            */
+  KDA_E_UNSUPPORTED = 6, /* a size the library has no kernel for (e.g. K > 128)          */
   KDA_E_WORKSPACE = 7,   /* workspace missing or smaller than kda_chunk_prefill_workspace_size */
   KDA_E_ALIAS = 8,       /* an output overlaps an input or another output               */
   KDA_E_HIP = 9          /* the HIP runtime reported an error                           */
