@@ -391,8 +391,8 @@ def bench_ckpt(args, dev, interval: int = 1024):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=41)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -523,7 +523,8 @@ def main():
                  "frac_bf16_dense_peak": flops / (c_avg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
         "attainable": {"t_roof_ms": t_roof * 1e3, "t_meas_ms": c_avg,
                        "frac": t_roof / (c_avg * 1e-3), "bound": "hbm" if t_hbm >= t_mfma else "mfma"},
-        "samples_ms": {"gather": g_ms, "chunk_prefill": c_ms, "scatter": s_ms},
+        "samples_ms": {k: [round(x, 4) for x in v] for k, v in (("gather", g_ms), ("chunk_prefill", c_ms),
+                                                                ("scatter", s_ms))},
         "percentiles_ms": {"gather": pct(g_ms), "chunk_prefill": pct(c_ms), "scatter": pct(s_ms)},
         "sources_sha256": {os.path.basename(f): sha256_file(f)[:16] for f in SOURCES},
         "gpu": torch.cuda.get_device_name(0),
