@@ -722,8 +722,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
       const float tot = pre[NW];
       const float ref = mw == 32 / RPW ? pre[32 / RPW] : pre[16 / RPW];
       float off = pre[0];
-#pragma unroll
-      for (int ww = 1; ww < NW; ++ww) off = w == ww ? pre[ww] : off;
+      off = pre[w];  // uniform index: one indexed register move
       gm[cc] = ref * kLog2e;
       gL[cc] = tot * kLog2e;
 #pragma unroll
