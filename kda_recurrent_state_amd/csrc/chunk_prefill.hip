@@ -57,6 +57,7 @@ constexpr int kC = 64;  // chunk length
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRangeLimit = 100.f;
 constexpr float kL2Eps = 1e-6f;
+constexpr float kL2EpsLane = kL2Eps / 64;  // each lane's share of eps in a 64-lane row sum
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -623,19 +624,20 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
           vx[r][vv] = __uint_as_float(raw.v[r][vv]);
       }
     }
-    // squared row norms of k and q (bf16 pairs: one dot2 per pair)
+    // squared row norms of k and q (bf16 pairs: one dot2 per pair), each lane
+    // adding its share of eps
     float sk[RPW], sq[RPW];
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       if (kBF16 && CPL == 2) {
         typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
         sk[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, raw.k[r][0]),
-                                                __builtin_bit_cast(bf16x2, raw.k[r][0]), 0.f, false);
+                                                __builtin_bit_cast(bf16x2, raw.k[r][0]), kL2EpsLane, false);
         sq[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, raw.q[r][0]),
-                                                __builtin_bit_cast(bf16x2, raw.q[r][0]), 0.f, false);
+                                                __builtin_bit_cast(bf16x2, raw.q[r][0]), kL2EpsLane, false);
       } else {
-        sk[r] = 0.f;
-        sq[r] = 0.f;
+        sk[r] = kL2EpsLane;
+        sq[r] = kL2EpsLane;
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) {
           sk[r] += kx[r][cc] * kx[r][cc];
@@ -660,8 +662,8 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
         }
 #pragma unroll
         for (int vv = 0; vv < VPL; ++vv) vx[r][vv] = (okr && vc_lo + vv < V && !p.v_zero) ? vx[r][vv] : 0.f;
-        sk[r] = 0.f;
-        sq[r] = 0.f;
+        sk[r] = kL2EpsLane;
+        sq[r] = kL2EpsLane;
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) {
           sk[r] += kx[r][cc] * kx[r][cc];
@@ -697,8 +699,8 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     if (p.l2norm) {
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
-        rk[r] = __frsqrt_rn(wave_sum(sk[r]) + kL2Eps);
-        rq[r] = __frsqrt_rn(wave_sum(sq[r]) + kL2Eps);
+        rk[r] = __frsqrt_rn(wave_sum(sk[r]));
+        rq[r] = __frsqrt_rn(wave_sum(sq[r]));
       }
     } else {
 #pragma unroll
