@@ -128,8 +128,8 @@ __device__ __forceinline__ float ld_in(const void* p, int64_t i) {
 }
 
 // Cross-lane reductions: DPP within each 16-lane row (quad swaps, half-row and
-// row mirrors), then the four row results combined through readlane.  Every
-// lane ends with the same bits.
+// row mirrors), then across rows by row broadcasts or the gfx950 half- and
+// quarter-wave swaps, and readlane.  Every lane ends with the same bits.
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, false));
@@ -147,14 +147,42 @@ __device__ __forceinline__ float dpp_rows(float x) {
                             __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, kRowMask, 0xF, false));
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
-  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
-  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
-  x += dpp<0x141>(x);  // row_half_mirror
-  x += dpp<0x140>(x);  // row_mirror: every lane of a row holds the row sum
-  x += dpp_rows<0x142, 0xA>(x);  // row_bcast:15: rows 1, 3 add rows 0, 2
-  x += dpp_rows<0x143, 0xC>(x);  // row_bcast:31: rows 2, 3 add rows 0 + 1
-  return lane_f(x, 63);
+// out[r] = 1 / sqrt(sum over the wave's 64 lanes of x[r]) for R rows at once,
+// the same bits in every lane.  Reduce-scatter: the half-wave swap pairs row j
+// with row j + R/2 (lanes 0-31 keep row j, lanes 32-63 row j + R/2), the
+// quarter-wave swap pairs those sums again, so each 16-lane group holds one
+// row of every register; DPP finishes the sums inside the groups, one rsqrt
+// per register covers four rows, and readlane hands each row to the wave.
+template <int R>
+__device__ __forceinline__ void rows_rsqrt(const float (&x)[R], float (&out)[R]) {
+  static_assert(R % 4 == 0, "rows");
+  constexpr int R2 = R / 2, R4 = R / 4;
+  float t[R2], u[R4];
+#pragma unroll
+  for (int j = 0; j < R2; ++j) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x[j]),
+                                                     __builtin_bit_cast(unsigned, x[j + R2]), false, false);
+    const unsigned lo = sw[0], hi = sw[1];  // scalar copies before the bit casts
+    t[j] = __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
+  }
+#pragma unroll
+  for (int j = 0; j < R4; ++j) {
+    const auto sw = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, t[j]),
+                                                     __builtin_bit_cast(unsigned, t[j + R4]), false, false);
+    const unsigned lo = sw[0], hi = sw[1];
+    u[j] = __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
+  }
+#pragma unroll
+  for (int j = 0; j < R4; ++j) {
+    u[j] += dpp<0xB1>(u[j]);   // quad_perm [1,0,3,2]
+    u[j] += dpp<0x4E>(u[j]);   // quad_perm [2,3,0,1]
+    u[j] += dpp<0x141>(u[j]);  // row_half_mirror
+    u[j] += dpp<0x140>(u[j]);  // row_mirror: every lane of a group holds the group's row
+    u[j] = __frsqrt_rn(u[j]);
+  }
+  // group g of u[j] holds row j + g * R4
+#pragma unroll
+  for (int r = 0; r < R; ++r) out[r] = lane_f(u[r % R4], 16 * (r / R4));
 }
 
 // (for x >= 0: rows outside the broadcast masks receive 0)
@@ -697,11 +725,8 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     // 1 / |row| for q and k (1 without l2norm; uniform branch)
     float rk[RPW], rq[RPW];
     if (p.l2norm) {
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        rk[r] = __frsqrt_rn(wave_sum(sk[r]));
-        rq[r] = __frsqrt_rn(wave_sum(sq[r]));
-      }
+      rows_rsqrt(sk, rk);
+      rows_rsqrt(sq, rq);
     } else {
 #pragma unroll
       for (int r = 0; r < RPW; ++r) rk[r] = rq[r] = 1.f;
