@@ -983,27 +983,42 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     lds_barrier();
 
     // ---------------- phase E: the serial chain on this wave's 16 columns ----
-    // V_new = U - W S, O = Qg S + A_qk V_new, S = D S + Kbar^T V_new
+    // V_new = U - W S, O = Qg S + A_qk V_new, S = D S + Kbar^T V_new.  Each
+    // product reads its LDS operands ahead of the MFMAs that use them, so the
+    // read latency overlaps the MFMAs already issued.
     bf16x8 bS[C::KS];
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) bS[ks] = pack_perm(S[2 * ks], S[2 * ks + 1]);
-    // Contraction step outer, row tile inner: the four accumulators of each
-    // product advance together, so consecutive MFMAs are independent.
+    // 2^gamma_L of this lane's state rows, read now so that the reads overlap V_new
+    f32x4 dec[C::KT];
+#pragma unroll
+    for (int ct = 0; ct < C::KT; ++ct) dec[ct] = *reinterpret_cast<const f32x4*>(sDec + 16 * ct + 4 * lg);
+    // V_new: contraction step outer, row tile inner (the four accumulators
+    // advance together, so consecutive MFMAs are independent); the next
+    // step's four operands are read before this step's MFMAs
     f32x4 Vn[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) Vn[rt] = U[rt];
+    {
+      bf16x8 a[2][4];
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      bf16x8 a[4];
+      for (int rt = 0; rt < 4; ++rt) a[0][rt] = ld_perm(sW + (16 * rt + lr) * C::LDKE + 4 * lg);
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) a[rt] = ld_perm(sW + (16 * rt + lr) * C::LDKE + 32 * ks + 4 * lg);
+      for (int ks = 0; ks < C::KS; ++ks) {
+        if (ks + 1 < C::KS) {
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) Vn[rt] = mfma(a[rt], bS[ks], Vn[rt]);
+          for (int rt = 0; rt < 4; ++rt)
+            a[(ks + 1) & 1][rt] = ld_perm(sW + (16 * rt + lr) * C::LDKE + 32 * (ks + 1) + 4 * lg);
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) Vn[rt] = mfma(a[ks & 1][rt], bS[ks], Vn[rt]);
+      }
     }
     bf16x8 bV[2];
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) bV[q2] = pack_perm(Vn[2 * q2], Vn[2 * q2 + 1]);
-    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ct = 0; ct < C::KT; ++ct) S[ct] *= dec[ct];
     // The output is computed transposed, O^T = S^T Qg^T + V_new^T A_qk^T (the
     // operands of each product swapped): tile rt then holds, per lane, the
     // four consecutive value columns 16w + 4lg.. of token 16rt + lr.
@@ -1011,30 +1026,49 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) O[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (kOut) {
+      bf16x8 a[2][4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) a[0][rt] = ld_perm(sQg + (16 * rt + lr) * C::LDKE + 4 * lg);
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
-        bf16x8 a[4];
+        if (ks + 1 < C::KS) {
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) a[rt] = ld_perm(sQg + (16 * rt + lr) * C::LDKE + 32 * ks + 4 * lg);
+          for (int rt = 0; rt < 4; ++rt)
+            a[(ks + 1) & 1][rt] = ld_perm(sQg + (16 * rt + lr) * C::LDKE + 32 * (ks + 1) + 4 * lg);
+        }
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) O[rt] = mfma(bS[ks], a[rt], O[rt]);
+        for (int rt = 0; rt < 4; ++rt) O[rt] = mfma(bS[ks], a[ks & 1][rt], O[rt]);
+      }
+      // the six A_qk tiles on or below the diagonal, (q2, rt) with 32 q2 <= 16 rt + 15
+      bf16x8 aq[6];
+#pragma unroll
+      for (int t = 0; t < 6; ++t) {
+        const int q2 = t < 4 ? 0 : 1, rt = t < 4 ? t : t - 2;
+        aq[t] = ld_perm(sAqk + (16 * rt + lr) * C::LDT + 32 * q2 + 4 * lg);
       }
 #pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          if (32 * q2 > 16 * rt + 15) continue;
-          O[rt] = mfma(bV[q2], ld_perm(sAqk + (16 * rt + lr) * C::LDT + 32 * q2 + 4 * lg), O[rt]);
-        }
+      for (int t = 0; t < 6; ++t) {
+        const int q2 = t < 4 ? 0 : 1, rt = t < 4 ? t : t - 2;
+        O[rt] = mfma(bV[q2], aq[t], O[rt]);
+      }
     }
-    __builtin_amdgcn_sched_barrier(0);
+    // S update: a ring of four Kbar^T operands in flight
+    {
+      constexpr int NU = 2 * C::KT;  // (q2, ct) steps, q2 outer
+      bf16x8 kr[4];
 #pragma unroll
-    for (int ct = 0; ct < C::KT; ++ct) S[ct] *= *reinterpret_cast<const f32x4*>(sDec + 16 * ct + 4 * lg);
+      for (int t = 0; t < 4; ++t)
+        kr[t] = ld_perm(sKB + (16 * (t % C::KT) + lr) * C::LDT + 32 * (t / C::KT) + 4 * lg);
 #pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2)
-#pragma unroll
-      for (int ct = 0; ct < C::KT; ++ct)
-        S[ct] = mfma(ld_perm(sKB + (16 * ct + lr) * C::LDT + 32 * q2 + 4 * lg), bV[q2], S[ct]);
+      for (int t = 0; t < NU; ++t) {
+        const int q2 = t / C::KT, ct = t % C::KT;
+        S[ct] = mfma(kr[t & 3], bV[q2], S[ct]);
+        if (t + 4 < NU) {
+          const int q2n = (t + 4) / C::KT, ctn = (t + 4) % C::KT;
+          kr[t & 3] = ld_perm(sKB + (16 * ctn + lr) * C::LDT + 32 * q2n + 4 * lg);
+        }
+      }
+    }
 
     // ---------------- output rows of this chunk ---------------------------
     if constexpr (!kOut) {
