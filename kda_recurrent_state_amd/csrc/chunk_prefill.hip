@@ -36,8 +36,9 @@
 //  * All dense contractions use v_mfma_f32_16x16x32_bf16 with fp32
 //    accumulation.  A C-layout accumulator holds 4 consecutive rows per lane;
 //    two such tiles give the 8 contraction values a B-operand lane needs, so a
-//    product's C-layout result feeds the next product directly, with the A
-//    operand read from LDS in the matching (permuted) k order.
+//    product's C-layout result feeds the next product directly; the LDS tiles
+//    that meet such operands store their contraction index in the matching
+//    permuted order, so each lane reads its 8 values as one 16-byte run.
 //  * Gate factors 2^(gamma_i - gamma_j) are split around a reference row m of
 //    the chunk: 2^(gamma_i - gamma_m) * 2^(gamma_m - gamma_j), one exp2 per
 //    (row, channel) for each side.  A chunk whose factors would leave the
@@ -76,17 +77,23 @@ struct Cfg {
   static constexpr int VPL = BV / 64;      // value columns per lane, elementwise phase
   static constexpr int KT = KP / 16;       // 16-row key tiles
   static constexpr int KS = KP / 32;       // 32-deep contraction steps over the key dim
-  // Row strides (bf16 elements), chosen so the lanes of one LDS pass hit
-  // distinct banks: tiles read 16 bytes per lane use a stride of 4 (mod 32)
-  // dwords, tiles read 8 bytes per lane a stride of 2 (mod 32) dwords.
-  static constexpr int LDK = KP + 8;       // [64][KP] tiles read 16 B/lane (KL, QL, KR)
-  static constexpr int LDKE = KP + 4;      // [64][KP] tiles read 8 B/lane (Qg, -W)
-  static constexpr int LDT = kC + 4;       // [X][64] tiles, read 8 B/lane
+  // Row strides (bf16 elements).  On gfx950, 16 rows read at 4 column offsets
+  // hit distinct LDS banks when the stride is 8 (mod 32) dwords for 16-byte
+  // reads and 2 (mod 4) dwords for 8-byte reads, and conflict-free 16-byte
+  // reads move about twice the bytes per clock of 8-byte reads (measured), so
+  // the tiles the serial chain reads as MFMA operands are read 16 bytes per
+  // lane: Qg and -W at stride LDK, A_qk at LDA, Kbar^T unpadded with a
+  // swizzle (kb_pos).
+  static constexpr int LDK = KP + 16;      // [64][KP] tiles (KL, QL, KR, Qg, -W)
+  static constexpr int LDT = kC + 4;       // [X][64] tiles read 8 B/lane (KE, (beta V)^T, A_kk)
+  static constexpr int LDA = kC + 16;      // A_qk [64][64]
   static constexpr int LDO = BV + 8;       // row stride (bf16) of the output staging tile
   static constexpr int SZ_ROW = kC * LDK * 2;
   static constexpr int SZ_KT = KP * LDT * 2;
   static constexpr int SZ_VT = BV * LDT * 2;
   static constexpr int SZ_T = kC * LDT * 2;
+  static constexpr int SZ_A = kC * LDA * 2;
+  static constexpr int SZ_KB = KP * kC * 2;  // Kbar^T: unpadded rows, 16-byte runs swizzled (kb_pos)
   // LDS map (bytes).  KL, QL and KR die after the A products; QL's space is
   // reused for -W and KR's for the output staging tile.
   static constexpr int R_KL = 0;                    // KL [64][KP]
@@ -95,15 +102,15 @@ struct Cfg {
   static constexpr int R_QG = R_KR + SZ_ROW;        // Qg [64][KP]
   static constexpr int R_KE = R_QG + SZ_ROW;        // (beta K 2^gamma)^T [KP][64]
   static constexpr int R_KB = R_KE + SZ_KT;         // Kbar^T [KP][64]
-  static constexpr int R_VT = R_KB + SZ_KT;         // (beta V)^T [BV][64]
+  static constexpr int R_VT = R_KB + SZ_KB;         // (beta V)^T [BV][64]
   static constexpr int R_AB = R_VT + SZ_VT;         // bf16 [64][LDT]: -A_kk below the diagonal blocks, D_b on them
   // fp32 diagonal blocks of A_kk, column-major: element (row, col) of block b
   // at b * AD_B + col * AD_C + row (16-byte aligned columns, blocks on
   // different banks)
   static constexpr int AD_C = 20, AD_B = 16 * AD_C + 4;
   static constexpr int R_AD = R_AB + SZ_T;
-  static constexpr int R_AQK = R_AD + 4 * AD_B * 4;  // A_qk bf16 [64][LDT]
-  static constexpr int R_TOT = R_AQK + SZ_T;        // per-wave gate sums fp32 [NW][KP]
+  static constexpr int R_AQK = R_AD + 4 * AD_B * 4;  // A_qk bf16 [64][LDA]
+  static constexpr int R_TOT = R_AQK + SZ_A;        // per-wave gate sums fp32 [NW][KP]
   static constexpr int R_DEC = R_TOT + NW * KP * 4; // 2^gamma_L fp32 [KP]
   static constexpr int R_RED = R_DEC + KP * 4;      // range guard fp32 [NW]
   static constexpr int LDS = R_RED + 64;
@@ -200,12 +207,22 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f3
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// 8 bf16 from two 4-element runs: k-slots 0..3 <- p[0..3], 4..7 <- p[16..19].
-// Matches the contraction order of pack_perm on two row-adjacent C tiles.
-__device__ __forceinline__ bf16x8 ld_perm(const __bf16* p) {
-  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
-  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
-  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+// Storage position of contraction index c in the tiles read as 16-byte MFMA
+// operands (Qg and -W over key channels, A_qk over tokens): within each
+// 32-block, c = 16h + 4g + j is stored at 8g + 4h + j, so the eight values
+// lane group g needs for one product (the k order pack_perm gives the other
+// operand) are one contiguous 16-byte run.  Runs of 4 from a multiple of 4
+// stay contiguous.
+__device__ __forceinline__ int kpos(int c) { return (c & ~31) | ((c & 12) << 1) | ((c & 16) >> 2) | (c & 3); }
+
+// Position of token t of row r in Kbar^T: rows of 64 tokens in kpos order
+// with no padding, the 16-byte run index XORed with bits 1-3 of the row.
+// The 16 rows x 4 runs of a 16-byte operand read then fall on distinct
+// banks, and the 8-byte transposed writes of rows 2l, 2l + 1 meet at most
+// 2 to a bank.
+__device__ __forceinline__ int kb_pos(int r, int t) {
+  const int p = kpos(t);
+  return r * kC + ((((p >> 3) ^ (r >> 1)) & 7) << 3) + (p & 7);
 }
 
 __device__ __forceinline__ bf16x8 pack_perm(const f32x4& lo, const f32x4& hi) {
@@ -400,7 +417,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
   if constexpr (kOut) {
     for (int e = tid; e < kC * kC; e += NT) {
       const int r = e >> 6, c = e & 63;
-      if ((c >> 4) > (r >> 4)) sAqk[r * C::LDT + c] = (__bf16)0.f;
+      if ((c >> 4) > (r >> 4)) sAqk[r * C::LDA + kpos(c)] = (__bf16)0.f;
     }
   }
 
@@ -801,14 +818,14 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
           *reinterpret_cast<bf16x2*>(sKR + i * C::LDK + c_lo) = bf16x2{kr[0], kr[CPL - 1]};
           if constexpr (kOut) {
             *reinterpret_cast<bf16x2*>(sQL + i * C::LDK + c_lo) = bf16x2{ql[0], ql[CPL - 1]};
-            *reinterpret_cast<bf16x2*>(sQg + i * C::LDKE + c_lo) = bf16x2{qg[0], qg[CPL - 1]};
+            *reinterpret_cast<bf16x2*>(sQg + i * C::LDK + kpos((int)c_lo)) = bf16x2{qg[0], qg[CPL - 1]};
           }
         } else {
           sKL[i * C::LDK + c_lo] = kl[0];
           sKR[i * C::LDK + c_lo] = kr[0];
           if constexpr (kOut) {
             sQL[i * C::LDK + c_lo] = ql[0];
-            sQg[i * C::LDKE + c_lo] = qg[0];
+            sQg[i * C::LDK + kpos((int)c_lo)] = qg[0];
           }
         }
       }
@@ -816,7 +833,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
 #pragma unroll
       for (int cc = 0; cc < CPL; ++cc) {
         bf16x4* pe = reinterpret_cast<bf16x4*>(sKE + (c_lo + cc) * C::LDT + RPW * w);
-        bf16x4* pb = reinterpret_cast<bf16x4*>(sKB + (c_lo + cc) * C::LDT + RPW * w);
+        const int rb = (int)c_lo + cc;
 #pragma unroll
         for (int h4 = 0; h4 < RPW / 4; ++h4) {
           bf16x4 xe, xb;
@@ -826,7 +843,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
             xb[j] = kb[cc][4 * h4 + j];
           }
           pe[h4] = xe;
-          pb[h4] = xb;
+          *reinterpret_cast<bf16x4*>(sKB + kb_pos(rb, RPW * w + 4 * h4)) = xb;
         }
       }
     }
@@ -846,8 +863,9 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
 
     // ---------------- phase B: A_kk (fp32) and A_qk (bf16) -----------------
     // 10 lower 16x16 block pairs (bi >= bj), round-robin over waves; A_kk and
-    // A_qk of a pair share the right operand, and a wave's pairs run as
-    // interleaved independent accumulator chains.
+    // A_qk of a pair share the key operand, and a wave's pairs run as
+    // interleaved independent accumulator chains.  A_qk is taken transposed
+    // (K Q^T) so that each lane holds four consecutive columns of one row.
     {
       constexpr int MP = (10 + NW - 1) / NW;  // pairs per wave at most
       f32x4 akk[MP], aqk[MP];
@@ -866,7 +884,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
             const int bj = pr - (bi * (bi + 1)) / 2;
             const bf16x8 rgt = ld8(sKR + (16 * bj + lr) * C::LDK + 32 * ks + 8 * lg);
             akk[m] = mfma(ld8(sKL + (16 * bi + lr) * C::LDK + 32 * ks + 8 * lg), rgt, akk[m]);
-            if constexpr (kOut) aqk[m] = mfma(ld8(sQL + (16 * bi + lr) * C::LDK + 32 * ks + 8 * lg), rgt, aqk[m]);
+            if constexpr (kOut) aqk[m] = mfma(rgt, ld8(sQL + (16 * bi + lr) * C::LDK + 32 * ks + 8 * lg), aqk[m]);
           }
         }
 #pragma unroll
@@ -879,8 +897,13 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int row = 16 * bi + 4 * lg + e;
-            if constexpr (kOut) sAqk[row * C::LDT + col] = (__bf16)(row >= col ? aqk[m][e] : 0.f);
             if (bi != bj) sAb[row * C::LDT + col] = (__bf16)(-akk[m][e]);
+          }
+          if constexpr (kOut) {  // row 16bi + lr, columns 16bj + 4lg + e
+            const int i = 16 * bi + lr, j0 = 16 * bj + 4 * lg;
+            *reinterpret_cast<bf16x4*>(sAqk + i * C::LDA + kpos(j0)) =
+                bf16x4{(__bf16)(i >= j0 ? aqk[m][0] : 0.f), (__bf16)(i >= j0 + 1 ? aqk[m][1] : 0.f),
+                       (__bf16)(i >= j0 + 2 ? aqk[m][2] : 0.f), (__bf16)(i >= j0 + 3 ? aqk[m][3] : 0.f)};
           }
           if (bi == bj) {  // rows 4lg..4lg+3 of column lr: one 16-byte store
             f32x4 d;
@@ -933,10 +956,13 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     //   X_b = D_b (R_b - sum_{c<b} A_bc X_c),  b = 0..3
     // R is read from the transposed tiles (4 consecutive rows per lane = C layout).
     // The wave's key-column tiles (-> W) and its own value tile (-> U) are
-    // solved together, as independent interleaved chains.
+    // solved together, as independent interleaved chains.  Each W block is
+    // also taken transposed (same operands swapped) so that a lane holds four
+    // consecutive channels of one token for the -W store.
     constexpr int NWT = (C::KT + NW - 1) / NW;  // W tiles per wave at most
     f32x4 X[NWT + 1][4];
     {
+      f32x4 Xt[NWT][4];
       const __bf16* rhs[NWT + 1];
       bool on[NWT + 1];
 #pragma unroll
@@ -962,8 +988,10 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
         const s16x4 d = ld4s(sAb + (16 * bk + lr) * C::LDT + 16 * bk + 4 * lg);
 #pragma unroll
         for (int m = 0; m <= NWT; ++m) {
-          X[m][bk] = mfma16(d, pack4(acc[m]), f32x4{0.f, 0.f, 0.f, 0.f});
+          const s16x4 r = pack4(acc[m]);
+          X[m][bk] = mfma16(d, r, f32x4{0.f, 0.f, 0.f, 0.f});
           xb[m][bk] = pack4(X[m][bk]);
+          if (m < NWT) Xt[m][bk] = mfma16(r, d, f32x4{0.f, 0.f, 0.f, 0.f});
         }
       }
       // -W into LDS (QL is dead)
@@ -973,8 +1001,9 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
         if (on[m]) {
 #pragma unroll
           for (int bk = 0; bk < 4; ++bk)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sW[(16 * bk + 4 * lg + e) * C::LDKE + 16 * ct + lr] = (__bf16)(-X[m][bk][e]);
+            *reinterpret_cast<bf16x4*>(sW + (16 * bk + lr) * C::LDK + kpos(16 * ct + 4 * lg)) =
+                bf16x4{(__bf16)(-Xt[m][bk][0]), (__bf16)(-Xt[m][bk][1]), (__bf16)(-Xt[m][bk][2]),
+                       (__bf16)(-Xt[m][bk][3])};
         }
       }
     }
@@ -1002,13 +1031,13 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     {
       bf16x8 a[2][4];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) a[0][rt] = ld_perm(sW + (16 * rt + lr) * C::LDKE + 4 * lg);
+      for (int rt = 0; rt < 4; ++rt) a[0][rt] = ld8(sW + (16 * rt + lr) * C::LDK + 8 * lg);
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
         if (ks + 1 < C::KS) {
 #pragma unroll
           for (int rt = 0; rt < 4; ++rt)
-            a[(ks + 1) & 1][rt] = ld_perm(sW + (16 * rt + lr) * C::LDKE + 32 * (ks + 1) + 4 * lg);
+            a[(ks + 1) & 1][rt] = ld8(sW + (16 * rt + lr) * C::LDK + 32 * (ks + 1) + 8 * lg);
         }
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) Vn[rt] = mfma(a[ks & 1][rt], bS[ks], Vn[rt]);
@@ -1028,13 +1057,13 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     if constexpr (kOut) {
       bf16x8 a[2][4];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) a[0][rt] = ld_perm(sQg + (16 * rt + lr) * C::LDKE + 4 * lg);
+      for (int rt = 0; rt < 4; ++rt) a[0][rt] = ld8(sQg + (16 * rt + lr) * C::LDK + 8 * lg);
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
         if (ks + 1 < C::KS) {
 #pragma unroll
           for (int rt = 0; rt < 4; ++rt)
-            a[(ks + 1) & 1][rt] = ld_perm(sQg + (16 * rt + lr) * C::LDKE + 32 * (ks + 1) + 4 * lg);
+            a[(ks + 1) & 1][rt] = ld8(sQg + (16 * rt + lr) * C::LDK + 32 * (ks + 1) + 8 * lg);
         }
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) O[rt] = mfma(bS[ks], a[ks & 1][rt], O[rt]);
@@ -1044,7 +1073,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
 #pragma unroll
       for (int t = 0; t < 6; ++t) {
         const int q2 = t < 4 ? 0 : 1, rt = t < 4 ? t : t - 2;
-        aq[t] = ld_perm(sAqk + (16 * rt + lr) * C::LDT + 32 * q2 + 4 * lg);
+        aq[t] = ld8(sAqk + (16 * rt + lr) * C::LDA + 32 * q2 + 8 * lg);
       }
 #pragma unroll
       for (int t = 0; t < 6; ++t) {
@@ -1055,17 +1084,19 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     // S update: a ring of four Kbar^T operands in flight
     {
       constexpr int NU = 2 * C::KT;  // (q2, ct) steps, q2 outer
+      // 16-byte run 4 q2 + lg of row 16 ct + lr (kb_pos; the swizzle depends on lr only)
+      const int kb0 = lr * kC + 8 * (lg ^ ((lr >> 1) & 7)), kb1 = lr * kC + 8 * ((4 + lg) ^ ((lr >> 1) & 7));
       bf16x8 kr[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        kr[t] = ld_perm(sKB + (16 * (t % C::KT) + lr) * C::LDT + 32 * (t / C::KT) + 4 * lg);
+        kr[t] = ld8(sKB + 16 * kC * (t % C::KT) + (t / C::KT ? kb1 : kb0));
 #pragma unroll
       for (int t = 0; t < NU; ++t) {
         const int q2 = t / C::KT, ct = t % C::KT;
         S[ct] = mfma(kr[t & 3], bV[q2], S[ct]);
         if (t + 4 < NU) {
           const int q2n = (t + 4) / C::KT, ctn = (t + 4) % C::KT;
-          kr[t & 3] = ld_perm(sKB + (16 * ctn + lr) * C::LDT + 32 * q2n + 4 * lg);
+          kr[t & 3] = ld8(sKB + 16 * kC * ctn + (q2n ? kb1 : kb0));
         }
       }
     }
