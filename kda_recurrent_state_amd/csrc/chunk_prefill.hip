@@ -318,8 +318,9 @@ struct Params {
   const int32_t* seq_cu;
 };
 
-// Raw bits of one chunk's inputs as loaded (bf16 pairs packed in one word),
-// kept in registers from the time the loads are issued until phase 0.
+// Raw bits of one chunk's inputs as loaded (bf16 pairs packed in one word, a
+// bf16 beta in the low half), kept in registers from the time the loads are
+// issued until phase 0.
 template <int RPW, int CPL, int VPL, bool kBF16>
 struct RawChunk {
   static constexpr int KW = (kBF16 && CPL == 2) ? 1 : CPL;  // words per row of q/k
@@ -499,7 +500,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
       }
       if (p.beta_bf16) {
 #pragma unroll
-        for (int r = 0; r < RPW; ++r) raw.b[r] = (unsigned)ld_at<unsigned short>(bb, 2 * ri[r]) << 16;
+        for (int r = 0; r < RPW; ++r) raw.b[r] = ld_at<unsigned short>(bb, 2 * ri[r]);
       } else {
 #pragma unroll
         for (int r = 0; r < RPW; ++r) raw.b[r] = ld_at<unsigned>(bb, 4 * ri[r]);
@@ -550,7 +551,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
       }
       if (p.beta_bf16) {
 #pragma unroll
-        for (int r = 0; r < RPW; ++r) raw.b[r] = (unsigned)static_cast<const unsigned short*>(p.beta)[th[r]] << 16;
+        for (int r = 0; r < RPW; ++r) raw.b[r] = static_cast<const unsigned short*>(p.beta)[th[r]];
       } else {
 #pragma unroll
         for (int r = 0; r < RPW; ++r) raw.b[r] = static_cast<const unsigned*>(p.beta)[th[r]];
@@ -642,6 +643,12 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     // The chunk's rows were loaded by issue_loads (for this chunk's start) while
     // the previous chunk computed; unpack them and zero what lies outside.
     float kx[RPW][CPL], qx[RPW][CPL], gx[RPW][CPL], vx[RPW][VPL], bt[RPW];
+    // bf16 beta arrives as the raw 16 bits (widening at load time would make
+    // the load wait for its data right there)
+    if (p.beta_bf16) {
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) raw.b[r] <<= 16;
+    }
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       bt[r] = __uint_as_float(raw.b[r]);
@@ -728,7 +735,8 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
         pv[h4] = x;
       }
     }
-    // inclusive sum of g over this wave's rows
+    // inclusive sum of g over this wave's rows; the wave totals go to LDS
+    float tw[CPL];
 #pragma unroll
     for (int cc = 0; cc < CPL; ++cc) {
       float run = 0.f;
@@ -737,8 +745,12 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
         run += gx[r][cc];
         gx[r][cc] = run;
       }
-      sTot[w * KP + c_lo + cc] = run;
+      tw[cc] = run;
     }
+    if (CPL == 2)
+      *reinterpret_cast<float2*>(sTot + w * KP + c_lo) = float2{tw[0], tw[CPL - 1]};
+    else
+      sTot[w * KP + c_lo] = tw[0];
     // 1 / |row| for q and k (1 without l2norm; uniform branch)
     float rk[RPW], rq[RPW];
     if (p.l2norm) {
@@ -754,15 +766,25 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     const int mw = (L > 32 ? 32 : 16) / RPW;  // waves whose rows precede the reference boundary
     float gm[CPL], gL[CPL];
     float guard = 0.f;
+    float totw[NW][CPL];  // every wave's totals of this lane's channels
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      if (CPL == 2) {
+        const float2 t2 = *reinterpret_cast<const float2*>(sTot + ww * KP + c_lo);
+        totw[ww][0] = t2.x;
+        totw[ww][CPL - 1] = t2.y;
+      } else {
+        totw[ww][0] = sTot[ww * KP + c_lo];
+      }
+    }
 #pragma unroll
     for (int cc = 0; cc < CPL; ++cc) {
-      const int64_t c = c_lo + cc;
       // prefix sums of the wave totals: off = before this wave, ref = before
       // the reference row, tot = the whole chunk (w and mw are uniform)
       float pre[NW + 1];
       pre[0] = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) pre[ww + 1] = pre[ww] + sTot[ww * KP + c];
+      for (int ww = 0; ww < NW; ++ww) pre[ww + 1] = pre[ww] + totw[ww][cc];
       const float tot = pre[NW];
       const float ref = mw == 32 / RPW ? pre[32 / RPW] : pre[16 / RPW];
       float off = pre[0];
@@ -1113,14 +1135,16 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
             bf16x4{(__bf16)O[rt][0], (__bf16)O[rt][1], (__bf16)O[rt][2], (__bf16)O[rt][3]};
       lds_barrier();
       constexpr int VPR = BV / 8;  // 16-byte runs per row
+      // uniform base at (token bos + t0, head h, column v0), 32-bit lane
+      // offsets (H * V <= 2^22 keeps them below 2^31 bytes)
+      char* const ob = static_cast<char*>(p.out) + (((bos + t0) * H + h) * V + v0) * 2;
+      const uint32_t row_b = (uint32_t)(H * V) * 2;
 #pragma unroll
       for (int u0 = 0; u0 < kC * VPR; u0 += NT) {
         const int u = u0 + tid_l;
         const int i = u / VPR, cv = u - i * VPR;
-        if (i < L && v0 + 8 * cv < V) {
-          const int64_t o = ((bos + t0 + i) * H + h) * V + v0 + 8 * cv;
-          *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(p.out) + o) = ld8(sO + i * C::LDO + 8 * cv);
-        }
+        if (i < L && v0 + 8 * cv < V)
+          *reinterpret_cast<bf16x8*>(ob + ((uint32_t)i * row_b + 16 * (uint32_t)cv)) = ld8(sO + i * C::LDO + 8 * cv);
       }
     } else {
       const int64_t vb = v0 + 16 * w + 4 * lg;  // this lane's first output column

@@ -119,6 +119,29 @@ def test_final_state_in_place(lengths, H, K, V, init_dtype):
     assert eo <= REL_TOL and ef <= REL_TOL
 
 
+@pytest.mark.parametrize("lengths,H,K,V", [
+    ([70, 130, 5], 2, 128, 128),   # vector loads
+    ([70, 33], 2, 33, 50),         # element-by-element loads
+])
+def test_bf16_beta(lengths, H, K, V):
+    """beta given in bf16 (its values rounded to bf16 in the oracle's input too)."""
+    import torch
+    import kda_recurrent_state_amd as kda
+    from tests.helpers import bf16_tensor
+    inp = wl.host_prefill_inputs(lengths, H, K, V, dtype="bf16", seed=sum(lengths) + K)
+    bits = wl.f32_to_bf16_bits(inp["beta"].astype(np.float32))
+    inp["beta"] = wl.bf16_bits_to_f32(bits).reshape(inp["beta"].shape)
+    print("case: bf16 beta lengths=%s H=%d K=%d V=%d" % (lengths, H, K, V), flush=True)
+    d = device_inputs(inp)
+    beta = bf16_tensor(bits).reshape(inp["beta"].shape)
+    o, f = kda.kda_chunk_prefill(d["q"], d["k"], d["v"], d["g"], beta, d["cu_seqlens"], initial_state=d["initial"])
+    torch.cuda.synchronize()
+    ro, rf = _ref(inp)
+    eo, ef = rel_l2(tensor_f64(o), ro), rel_l2(tensor_f64(f), rf)
+    print("  relL2 out %.3e final %.3e" % (eo, ef), flush=True)
+    assert eo <= REL_TOL and ef <= REL_TOL
+
+
 def test_bf16_ragged_varlen():
     inp = wl.host_prefill_inputs([1, 17, 64, 65, 200, 333, 128], 4, 128, 128, dtype="bf16", seed=5)
     _check(inp)
