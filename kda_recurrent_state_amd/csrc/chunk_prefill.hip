@@ -51,6 +51,8 @@
 //    shared q/k/g tiles are served from one L2.
 #include "internal.h"
 
+#include <type_traits>
+
 namespace kda {
 namespace {
 
@@ -241,9 +243,18 @@ __device__ __forceinline__ f32x4 mfma16(const s16x4& a, const s16x4& b, const f3
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
+// Four floats to bf16, converted in pairs (one v_cvt_pk_bf16_f32 each; a
+// bf16x4 built element by element converts one at a time and permutes).
+__device__ __forceinline__ bf16x4 to_bf16x4(float a, float b, float c, float d) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 lo = bf16x2{(__bf16)a, (__bf16)b}, hi = bf16x2{(__bf16)c, (__bf16)d};
+  return __builtin_bit_cast(bf16x4, u32x2{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)});
+}
+
 __device__ __forceinline__ s16x4 pack4(const f32x4& x) {
-  return s16x4{__builtin_bit_cast(short, (__bf16)x[0]), __builtin_bit_cast(short, (__bf16)x[1]),
-               __builtin_bit_cast(short, (__bf16)x[2]), __builtin_bit_cast(short, (__bf16)x[3])};
+  const float a = x[0], b = x[1], c = x[2], d = x[3];  // scalar copies of the lanes' elements
+  return __builtin_bit_cast(s16x4, to_bf16x4(a, b, c, d));
 }
 
 __device__ __forceinline__ s16x4 ld4s(const __bf16* p) { return *reinterpret_cast<const s16x4*>(p); }
@@ -343,7 +354,7 @@ __device__ __forceinline__ void store_state(const f32x4 (&S)[KT], void* dst, int
       const int64_t o = (row + vc) * K + c0;
       if (bf)
         *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(dst) + o) =
-            bf16x4{(__bf16)S[ct][0], (__bf16)S[ct][1], (__bf16)S[ct][2], (__bf16)S[ct][3]};
+            to_bf16x4(S[ct][0], S[ct][1], S[ct][2], S[ct][3]);
       else
         *reinterpret_cast<f32x4*>(static_cast<float*>(dst) + o) = S[ct];
     }
@@ -888,53 +899,70 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     // A_qk of a pair share the key operand, and a wave's pairs run as
     // interleaved independent accumulator chains.  A_qk is taken transposed
     // (K Q^T) so that each lane holds four consecutive columns of one row.
+    // The pair count is uniform per wave, so each count has its own
+    // branch-free body whose operand reads run one contraction step ahead.
     {
-      constexpr int MP = (10 + NW - 1) / NW;  // pairs per wave at most
-      f32x4 akk[MP], aqk[MP];
+      auto pairs = [&](auto npc) {
+        constexpr int NP = decltype(npc)::value;
+        int bi[NP], bj[NP];
 #pragma unroll
-      for (int m = 0; m < MP; ++m) {
-        akk[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        aqk[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-        for (int m = 0; m < MP; ++m) {
+        for (int m = 0; m < NP; ++m) {
           const int pr = w + m * NW;
-          if (pr < 10) {
-            const int bi = pr >= 6 ? 3 : (pr >= 3 ? 2 : (pr >= 1 ? 1 : 0));
-            const int bj = pr - (bi * (bi + 1)) / 2;
-            const bf16x8 rgt = ld8(sKR + (16 * bj + lr) * C::LDK + 32 * ks + 8 * lg);
-            akk[m] = mfma(ld8(sKL + (16 * bi + lr) * C::LDK + 32 * ks + 8 * lg), rgt, akk[m]);
-            if constexpr (kOut) aqk[m] = mfma(rgt, ld8(sQL + (16 * bi + lr) * C::LDK + 32 * ks + 8 * lg), aqk[m]);
+          bi[m] = pr >= 6 ? 3 : (pr >= 3 ? 2 : (pr >= 1 ? 1 : 0));
+          bj[m] = pr - (bi[m] * (bi[m] + 1)) / 2;
+        }
+        f32x4 akk[NP], aqk[NP];
+        bf16x8 oL[2][NP], oR[2][NP], oQ[2][NP];
+        auto fetch = [&](int ks, int bf) {
+#pragma unroll
+          for (int m = 0; m < NP; ++m) {
+            oR[bf][m] = ld8(sKR + (16 * bj[m] + lr) * C::LDK + 32 * ks + 8 * lg);
+            oL[bf][m] = ld8(sKL + (16 * bi[m] + lr) * C::LDK + 32 * ks + 8 * lg);
+            if constexpr (kOut) oQ[bf][m] = ld8(sQL + (16 * bi[m] + lr) * C::LDK + 32 * ks + 8 * lg);
+          }
+        };
+#pragma unroll
+        for (int m = 0; m < NP; ++m) {
+          akk[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+          aqk[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        fetch(0, 0);
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+          if (ks + 1 < C::KS) fetch(ks + 1, (ks + 1) & 1);
+#pragma unroll
+          for (int m = 0; m < NP; ++m) {
+            akk[m] = mfma(oL[ks & 1][m], oR[ks & 1][m], akk[m]);
+            if constexpr (kOut) aqk[m] = mfma(oR[ks & 1][m], oQ[ks & 1][m], aqk[m]);
           }
         }
 #pragma unroll
-      for (int m = 0; m < MP; ++m) {
-        const int pr = w + m * NW;
-        if (pr < 10) {
-          const int bi = pr >= 6 ? 3 : (pr >= 3 ? 2 : (pr >= 1 ? 1 : 0));
-          const int bj = pr - (bi * (bi + 1)) / 2;
-          const int col = 16 * bj + lr;
+        for (int m = 0; m < NP; ++m) {
+          const int col = 16 * bj[m] + lr;
+          if (bi[m] != bj[m]) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int row = 16 * bi + 4 * lg + e;
-            if (bi != bj) sAb[row * C::LDT + col] = (__bf16)(-akk[m][e]);
-          }
-          if constexpr (kOut) {  // row 16bi + lr, columns 16bj + 4lg + e
-            const int i = 16 * bi + lr, j0 = 16 * bj + 4 * lg;
-            *reinterpret_cast<bf16x4*>(sAqk + i * C::LDA + kpos(j0)) =
-                bf16x4{(__bf16)(i >= j0 ? aqk[m][0] : 0.f), (__bf16)(i >= j0 + 1 ? aqk[m][1] : 0.f),
-                       (__bf16)(i >= j0 + 2 ? aqk[m][2] : 0.f), (__bf16)(i >= j0 + 3 ? aqk[m][3] : 0.f)};
-          }
-          if (bi == bj) {  // rows 4lg..4lg+3 of column lr: one 16-byte store
+            for (int e = 0; e < 4; ++e) sAb[(16 * bi[m] + 4 * lg + e) * C::LDT + col] = (__bf16)(-akk[m][e]);
+          } else {  // rows 4lg..4lg+3 of column lr: one 16-byte store
             f32x4 d;
 #pragma unroll
             for (int e = 0; e < 4; ++e) d[e] = 4 * lg + e > lr ? akk[m][e] : 0.f;
-            *reinterpret_cast<f32x4*>(sAd + bi * C::AD_B + lr * C::AD_C + 4 * lg) = d;
+            *reinterpret_cast<f32x4*>(sAd + bi[m] * C::AD_B + lr * C::AD_C + 4 * lg) = d;
+          }
+          if constexpr (kOut) {  // row 16bi + lr, columns 16bj + 4lg + e
+            const int i = 16 * bi[m] + lr, j0 = 16 * bj[m] + 4 * lg;
+            *reinterpret_cast<bf16x4*>(sAqk + i * C::LDA + kpos(j0)) =
+                to_bf16x4(i >= j0 ? aqk[m][0] : 0.f, i >= j0 + 1 ? aqk[m][1] : 0.f, i >= j0 + 2 ? aqk[m][2] : 0.f,
+                          i >= j0 + 3 ? aqk[m][3] : 0.f);
           }
         }
-      }
+      };
+      constexpr int MP = (10 + NW - 1) / NW;  // pairs per wave at most
+      static_assert(MP >= 2 && MP <= 3, "pairs per wave");
+      const int np = (10 - w + NW - 1) / NW;  // this wave's pairs (uniform)
+      if (np == MP)
+        pairs(std::integral_constant<int, MP>{});
+      else
+        pairs(std::integral_constant<int, MP - 1>{});
     }
     lds_barrier();
 
@@ -1024,8 +1052,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
 #pragma unroll
           for (int bk = 0; bk < 4; ++bk)
             *reinterpret_cast<bf16x4*>(sW + (16 * bk + lr) * C::LDK + kpos(16 * ct + 4 * lg)) =
-                bf16x4{(__bf16)(-Xt[m][bk][0]), (__bf16)(-Xt[m][bk][1]), (__bf16)(-Xt[m][bk][2]),
-                       (__bf16)(-Xt[m][bk][3])};
+                to_bf16x4(-Xt[m][bk][0], -Xt[m][bk][1], -Xt[m][bk][2], -Xt[m][bk][3]);
         }
       }
     }
@@ -1132,7 +1159,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
         *reinterpret_cast<bf16x4*>(sO + (16 * rt + lr) * C::LDO + 16 * w + 4 * lg) =
-            bf16x4{(__bf16)O[rt][0], (__bf16)O[rt][1], (__bf16)O[rt][2], (__bf16)O[rt][3]};
+            to_bf16x4(O[rt][0], O[rt][1], O[rt][2], O[rt][3]);
       lds_barrier();
       constexpr int VPR = BV / 8;  // 16-byte runs per row
       // uniform base at (token bos + t0, head h, column v0), 32-bit lane
