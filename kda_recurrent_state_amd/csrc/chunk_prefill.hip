@@ -880,6 +880,12 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
         }
       }
     }
+    // The next chunk's loads: the first half of the waves (which the SIMD
+    // arbiter favours, so they finish phase A first) issue theirs now, while
+    // their SIMD partners finish phase A; the other half issue theirs after
+    // phase B, while wave 0 computes phase C.
+    const bool early = w < NW / 2;
+    if (early && t0 + L < len) issue_loads(t0 + L);
     lds_barrier();
     {
       // range guard of every wave (written before the barrier above): a span
@@ -890,6 +896,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
       for (int ww = 1; ww < NW; ++ww) gmax = fmaxf(gmax, sRed[ww]);
       if (gmax > kRangeLimit && L > 1) {
         Lcap = L > 16 ? 16 : (L > 4 ? 4 : 1);
+        if (early && t0 + L < len) issue_loads(t0);  // this chunk's rows again
         continue;
       }
     }
@@ -902,12 +909,14 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     // The pair count is uniform per wave, so each count has its own
     // branch-free body whose operand reads run one contraction step ahead.
     {
+      // rotated so that the extra pairs go to the waves that load after phase B
+      const int wr = w < NW / 2 ? w + NW / 2 : w - NW / 2;
       auto pairs = [&](auto npc) {
         constexpr int NP = decltype(npc)::value;
         int bi[NP], bj[NP];
 #pragma unroll
         for (int m = 0; m < NP; ++m) {
-          const int pr = w + m * NW;
+          const int pr = wr + m * NW;
           bi[m] = pr >= 6 ? 3 : (pr >= 3 ? 2 : (pr >= 1 ? 1 : 0));
           bj[m] = pr - (bi[m] * (bi[m] + 1)) / 2;
         }
@@ -958,7 +967,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
       };
       constexpr int MP = (10 + NW - 1) / NW;  // pairs per wave at most
       static_assert(MP >= 2 && MP <= 3, "pairs per wave");
-      const int np = (10 - w + NW - 1) / NW;  // this wave's pairs (uniform)
+      const int np = (10 - wr + NW - 1) / NW;  // this wave's pairs (uniform)
       if (np == MP)
         pairs(std::integral_constant<int, MP>{});
       else
@@ -966,8 +975,8 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     }
     lds_barrier();
 
-    // the next chunk's loads are issued now and land while phases C-E compute
-    if (t0 + L < len) issue_loads(t0 + L);
+    // the other half's loads (they land while phases C-E compute)
+    if (!early && t0 + L < len) issue_loads(t0 + L);
 
     // ---------------- phase C: D_b = (I + A_bb)^-1 for the diagonal blocks --
     if (w == 0) {
