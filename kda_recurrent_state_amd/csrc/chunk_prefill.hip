@@ -653,6 +653,41 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     // ---------------- phase 0: loads, (beta V)^T, gate sums, norms ----------
     // The chunk's rows were loaded by issue_loads (for this chunk's start) while
     // the previous chunk computed; unpack them and zero what lies outside.
+    // Rows past the chunk, channels past K and value columns past V were
+    // loaded clamped: zero their bits before anything is unpacked (a full
+    // chunk has none; uniform branch).  Masking the loaded words in place
+    // keeps a single unpack path after the branch.
+    if (!(L == kC && K == KP && v0 + BV <= V && !p.v_zero)) {
+      unsigned mk[Raw::KW], mv[Raw::VW];  // this lane's channel / column masks per word
+#pragma unroll
+      for (int cw = 0; cw < Raw::KW; ++cw) {
+        if (kBF16 && CPL == 2)
+          mk[cw] = (c_lo < K ? 0xffffu : 0u) | (c_lo + 1 < K ? 0xffff0000u : 0u);
+        else
+          mk[cw] = c_lo + cw < K ? ~0u : 0u;
+      }
+#pragma unroll
+      for (int vw = 0; vw < Raw::VW; ++vw) {
+        if (kBF16 && VPL == 2)
+          mv[vw] = p.v_zero ? 0u : ((vc_lo < V ? 0xffffu : 0u) | (vc_lo + 1 < V ? 0xffff0000u : 0u));
+        else
+          mv[vw] = (!p.v_zero && vc_lo + vw < V) ? ~0u : 0u;
+      }
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        const bool okr = RPW * w + r < L;  // uniform
+        raw.b[r] = okr ? raw.b[r] : 0u;
+#pragma unroll
+        for (int cw = 0; cw < Raw::KW; ++cw) {
+          raw.k[r][cw] = okr ? raw.k[r][cw] & mk[cw] : 0u;
+          raw.q[r][cw] = okr ? raw.q[r][cw] & mk[cw] : 0u;
+        }
+#pragma unroll
+        for (int vw = 0; vw < Raw::VW; ++vw) raw.v[r][vw] = okr ? raw.v[r][vw] & mv[vw] : 0u;
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) raw.g[r][cc] = (okr && c_lo + cc < K) ? raw.g[r][cc] : 0.f;
+      }
+    }
     float kx[RPW][CPL], qx[RPW][CPL], gx[RPW][CPL], vx[RPW][VPL], bt[RPW];
     // bf16 beta arrives as the raw 16 bits (widening at load time would make
     // the load wait for its data right there)
@@ -699,32 +734,6 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
         sq[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, raw.q[r][0]),
                                                 __builtin_bit_cast(bf16x2, raw.q[r][0]), kL2EpsLane, false);
       } else {
-        sk[r] = kL2EpsLane;
-        sq[r] = kL2EpsLane;
-#pragma unroll
-        for (int cc = 0; cc < CPL; ++cc) {
-          sk[r] += kx[r][cc] * kx[r][cc];
-          sq[r] += qx[r][cc] * qx[r][cc];
-        }
-      }
-    }
-    // Rows past the chunk, channels past K and value columns past V were
-    // loaded clamped: zero them (and redo the norms).  A full chunk has none
-    // (uniform branch).
-    if (!(L == kC && K == KP && v0 + BV <= V && !p.v_zero)) {
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        const bool okr = RPW * w + r < L;
-        bt[r] = okr ? bt[r] : 0.f;
-#pragma unroll
-        for (int cc = 0; cc < CPL; ++cc) {
-          const bool okc = okr && c_lo + cc < K;
-          kx[r][cc] = okc ? kx[r][cc] : 0.f;
-          qx[r][cc] = okc ? qx[r][cc] : 0.f;
-          gx[r][cc] = okc ? gx[r][cc] : 0.f;
-        }
-#pragma unroll
-        for (int vv = 0; vv < VPL; ++vv) vx[r][vv] = (okr && vc_lo + vv < V && !p.v_zero) ? vx[r][vv] : 0.f;
         sk[r] = kL2EpsLane;
         sq[r] = kL2EpsLane;
 #pragma unroll
@@ -896,7 +905,9 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
       for (int ww = 1; ww < NW; ++ww) gmax = fmaxf(gmax, sRed[ww]);
       if (gmax > kRangeLimit && L > 1) {
         Lcap = L > 16 ? 16 : (L > 4 ? 4 : 1);
-        if (early && t0 + L < len) issue_loads(t0);  // this chunk's rows again
+        // this chunk's rows again (the early half has overwritten them; reloading
+        // in every wave also ends the rows' live range at phase 0)
+        issue_loads(t0);
         continue;
       }
     }
