@@ -1029,33 +1029,41 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     // solved together, as independent interleaved chains.  Each W block is
     // also taken transposed (same operands swapped) so that a lane holds four
     // consecutive channels of one token for the -W store.
-    constexpr int NWT = (C::KT + NW - 1) / NW;  // W tiles per wave at most
+    constexpr int NWT = C::KT / NW;  // W tiles per wave
+    static_assert(C::KT % NW == 0, "every wave owns the same number of W tiles");
     f32x4 X[NWT + 1][4];
     {
       f32x4 Xt[NWT][4];
       const __bf16* rhs[NWT + 1];
-      bool on[NWT + 1];
 #pragma unroll
-      for (int m = 0; m < NWT; ++m) {
-        const int ct = w + m * NW;
-        on[m] = ct < C::KT;
-        rhs[m] = sKE + (16 * (on[m] ? ct : 0) + lr) * C::LDT;
-      }
-      on[NWT] = true;
+      for (int m = 0; m < NWT; ++m) rhs[m] = sKE + (16 * (w + m * NW) + lr) * C::LDT;
       rhs[NWT] = sVT + (16 * w + lr) * C::LDT;
+      // every operand of the substitution is read up front: the block rows of
+      // (I + A_kk)^-1's factors (A_bc below the diagonal, D_b on it) and the
+      // right-hand sides
+      s16x4 ab[4][4];
+      bf16x4 rb[NWT + 1][4];
+#pragma unroll
+      for (int bk = 0; bk < 4; ++bk) {
+#pragma unroll
+        for (int c = 0; c <= bk; ++c) ab[bk][c] = ld4s(sAb + (16 * bk + lr) * C::LDT + 16 * c + 4 * lg);
+#pragma unroll
+        for (int m = 0; m <= NWT; ++m) rb[m][bk] = *reinterpret_cast<const bf16x4*>(rhs[m] + 16 * bk + 4 * lg);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // all reads issued before the chain starts
       s16x4 xb[NWT + 1][4];
 #pragma unroll
       for (int bk = 0; bk < 4; ++bk) {
         f32x4 acc[NWT + 1];
 #pragma unroll
-        for (int m = 0; m <= NWT; ++m) acc[m] = widen4(rhs[m] + 16 * bk + 4 * lg);
+        for (int m = 0; m <= NWT; ++m)
+          acc[m] = f32x4{(float)rb[m][bk][0], (float)rb[m][bk][1], (float)rb[m][bk][2], (float)rb[m][bk][3]};
 #pragma unroll
         for (int c = 0; c < bk; ++c) {
-          const s16x4 a = ld4s(sAb + (16 * bk + lr) * C::LDT + 16 * c + 4 * lg);
 #pragma unroll
-          for (int m = 0; m <= NWT; ++m) acc[m] = mfma16(a, xb[m][c], acc[m]);
+          for (int m = 0; m <= NWT; ++m) acc[m] = mfma16(ab[bk][c], xb[m][c], acc[m]);
         }
-        const s16x4 d = ld4s(sAb + (16 * bk + lr) * C::LDT + 16 * bk + 4 * lg);
+        const s16x4 d = ab[bk][bk];
 #pragma unroll
         for (int m = 0; m <= NWT; ++m) {
           const s16x4 r = pack4(acc[m]);
@@ -1068,12 +1076,10 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
 #pragma unroll
       for (int m = 0; m < NWT; ++m) {
         const int ct = w + m * NW;
-        if (on[m]) {
 #pragma unroll
-          for (int bk = 0; bk < 4; ++bk)
-            *reinterpret_cast<bf16x4*>(sW + (16 * bk + lr) * C::LDK + kpos(16 * ct + 4 * lg)) =
-                to_bf16x4(-Xt[m][bk][0], -Xt[m][bk][1], -Xt[m][bk][2], -Xt[m][bk][3]);
-        }
+        for (int bk = 0; bk < 4; ++bk)
+          *reinterpret_cast<bf16x4*>(sW + (16 * bk + lr) * C::LDK + kpos(16 * ct + 4 * lg)) =
+              to_bf16x4(-Xt[m][bk][0], -Xt[m][bk][1], -Xt[m][bk][2], -Xt[m][bk][3]);
       }
     }
     // U for this wave's own value columns stays in registers
