@@ -184,8 +184,15 @@ def test_single_token():
 
 
 @pytest.mark.parametrize("gval", [-30.0, -1e4])
-def test_strong_decay_uses_shorter_chunks(gval):
-    inp = wl.host_prefill_inputs([150, 70], 2, 64, 64, dtype="bf16", seed=12)
+@pytest.mark.parametrize("lengths,H,K,V", [
+    ([150, 70], 2, 64, 64),                            # K <= 64 kernel
+    ([150, 70], 2, 128, 128),                          # 64-column value blocks (few chains)
+    ([130 + 5 * (i % 7) for i in range(64)], 8, 128, 128),  # 128-column value blocks (>= 512 chains)
+])
+def test_strong_decay_uses_shorter_chunks(gval, lengths, H, K, V):
+    """Gate factors past 2^+-100 make a chunk retry as shorter chunks, after
+    half the waves have already issued the next chunk's loads."""
+    inp = wl.host_prefill_inputs(lengths, H, K, V, dtype="bf16", seed=12)
     g = inp["g"].copy()
     g[::7, :, ::3] = gval          # some channels of some tokens decay (almost) to zero
     inp["g"] = g
