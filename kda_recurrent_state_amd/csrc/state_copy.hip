@@ -10,18 +10,23 @@
 // Design: the copy is HBM-bound, so each workgroup streams one contiguous
 // tile of one row with the widest vector the alignment allows (16 B when the
 // cache base, row stride, payload and packed base are all 16-byte aligned),
-// every thread keeping several independent 16-byte loads in flight before its
-// stores.  Loads and stores are non-temporal: the rows are touched once.
-// Invalid / flag-false gather rows only store zeros, scatter skips the whole
-// tile for an invalid target.  A grid-stride loop over (row, tile) pairs
-// keeps the grid within the dispatch limits for any selection size.
+// every thread keeping several independent loads in flight before its stores
+// (16-byte tiles: 8 KiB per workgroup for gather, 32 KiB for scatter).  Loads
+// and stores are non-temporal: the rows are touched once.  Invalid /
+// flag-false gather rows only store zeros, scatter skips the whole tile for an
+// invalid target.  A grid-stride loop over (row, tile) pairs keeps the grid
+// within the dispatch limits for any selection size.
 #include "internal.h"
 
 namespace kda {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 8;  // vectors in flight per thread
+// vectors in flight per thread: gather (strided rows in, dense packed rows
+// out) runs fastest with 8 KiB tiles, scatter (dense in, strided out) with
+// 32 KiB tiles
+constexpr int kGatherUnroll = 2;
+constexpr int kScatterUnroll = 8;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -31,7 +36,7 @@ __device__ __forceinline__ T zero_vec() {
   return T(0);
 }
 
-template <typename VecT, bool kGather, typename IdxT>
+template <typename VecT, bool kGather, typename IdxT, int kUnroll>
 __global__ __launch_bounds__(kThreads) void state_copy_kernel(char* __restrict__ cache, int64_t row_stride_bytes,
                                                                int64_t num_rows, int64_t payload_vecs,
                                                                int64_t tiles_per_row, int64_t total_tiles,
@@ -89,18 +94,18 @@ hipError_t launch_typed(bool gather, char* cache, int64_t row_stride_bytes, int6
                         const void* indices, int64_t num_selected, const uint8_t* flags, char* packed,
                         hipStream_t stream) {
   const int64_t payload_vecs = payload_bytes / (int64_t)sizeof(VecT);
-  const int64_t tile_vecs = (int64_t)kThreads * kUnroll;
+  const int64_t tile_vecs = (int64_t)kThreads * (gather ? kGatherUnroll : kScatterUnroll);
   const int64_t tiles_per_row = (payload_vecs + tile_vecs - 1) / tile_vecs;
   const int64_t total = tiles_per_row * num_selected;
   const int64_t max_grid = 1 << 20;
   const unsigned grid = (unsigned)(total < max_grid ? total : max_grid);
   const IdxT* idx = static_cast<const IdxT*>(indices);
   if (gather) {
-    hipLaunchKernelGGL((state_copy_kernel<VecT, true, IdxT>), dim3(grid), dim3(kThreads), 0, stream, cache,
-                       row_stride_bytes, num_rows, payload_vecs, tiles_per_row, total, idx, flags, packed);
+    hipLaunchKernelGGL((state_copy_kernel<VecT, true, IdxT, kGatherUnroll>), dim3(grid), dim3(kThreads), 0, stream,
+                       cache, row_stride_bytes, num_rows, payload_vecs, tiles_per_row, total, idx, flags, packed);
   } else {
-    hipLaunchKernelGGL((state_copy_kernel<VecT, false, IdxT>), dim3(grid), dim3(kThreads), 0, stream, cache,
-                       row_stride_bytes, num_rows, payload_vecs, tiles_per_row, total, idx, nullptr, packed);
+    hipLaunchKernelGGL((state_copy_kernel<VecT, false, IdxT, kScatterUnroll>), dim3(grid), dim3(kThreads), 0, stream,
+                       cache, row_stride_bytes, num_rows, payload_vecs, tiles_per_row, total, idx, nullptr, packed);
   }
   return hipGetLastError();
 }
