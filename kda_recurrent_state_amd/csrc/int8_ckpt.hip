@@ -67,6 +67,20 @@ __device__ __forceinline__ int encode(float x, float sc) {
   return (int)r;
 }
 
+// The same code from rc = 1 / sc (correctly rounded; 0 where sc = 0), for sc
+// in the normal range: z = x / sc lies in [-127.00001, 127.00001], and
+// q = x * rc is within |z| * 2^-23 * (1 + 2^-24) < 2^-16 of z, while the
+// correctly rounded quotient is within 2^-18 of z.  When q is at least 2^-14
+// away from every half-integer, both round to the same integer as z does;
+// otherwise the exact quotient decides (as in encode).
+__device__ __forceinline__ int encode_rcp(float x, float sc, float rc) {
+  const float q = x * rc;
+  float r = rintf(q);
+  if (fabsf(q - r) > 0.5f - 0x1p-14f) r = rintf(x / sc);
+  r = r > 127.f ? 127.f : (r < -127.f ? -127.f : r);
+  return (int)r;
+}
+
 typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
@@ -160,14 +174,24 @@ __global__ __launch_bounds__(kQThreads) void quantize_scatter_kernel(Int8Params 
   }
   __syncthreads();
   if (c0 >= K) return;
-  float sc[kQC];
+  float sc[kQC], rc[kQC];
+  bool tiny = false;  // a nonzero scale below the normal range of 1 / sc: exact quotients
 #pragma unroll
-  for (int t = 0; t < kQC; ++t) sc[t] = c0 + t < K ? scl[c0 + t] : 0.f;
+  for (int t = 0; t < kQC; ++t) {
+    sc[t] = c0 + t < K ? scl[c0 + t] : 0.f;
+    rc[t] = sc[t] == 0.f ? 0.f : 1.f / sc[t];
+    tiny |= sc[t] != 0.f && sc[t] < 0x1p-120f;
+  }
   auto store = [&](int row, const float (&x)[kQC]) {
     int8_t* dst = qd + (int64_t)row * K + c0;
     int qq[kQC];
+    if (tiny) {
 #pragma unroll
-    for (int t = 0; t < kQC; ++t) qq[t] = encode(x[t], sc[t]);
+      for (int t = 0; t < kQC; ++t) qq[t] = encode(x[t], sc[t]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < kQC; ++t) qq[t] = encode_rcp(x[t], sc[t], rc[t]);
+    }
     if (p.vec) {
       unsigned w[2] = {0u, 0u};
 #pragma unroll

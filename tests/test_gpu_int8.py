@@ -5,9 +5,10 @@ produced by kda_ckpt_dequantize_gather, must equal the oracle's bit for bit
 (the quantisation decisions are fp32 on both sides).  Slots not selected and
 the gaps between slots keep their bits.  Covers fp32/bf16 packed states,
 int32/int64 indices with invalid entries, flags, slot gaps, vector and
-element paths (K not a multiple of 8), V above 128, a full-size store of 256
-states of [32,128,128], and a prefill that resumes from dequantised
-checkpoints.
+element paths (K not a multiple of 8), V above 128, values next to the
+rounding boundaries of the codes with scales down to the subnormal range, a
+full-size store of 256 states of [32,128,128], and a prefill that resumes
+from dequantised checkpoints.
 """
 import numpy as np
 import pytest
@@ -133,6 +134,40 @@ def test_full_size_store():
     assert np.array_equal(back.cpu().numpy().view(np.uint32), oracle.int8_dequantize(rq, rs).view(np.uint32))
     rest = np.setdiff1d(np.arange(slots), sel)
     assert not bool(qd[torch.from_numpy(rest).cuda()].any())
+
+
+def test_codes_near_half_integers():
+    """Values within a few ulps of (k + 1/2) * scale, where the rounding of the
+    quotient decides the code, and scales from the subnormal range to 2^-120
+    and beyond: codes and scales bit-exact against the oracle."""
+    import torch
+    import kda_recurrent_state_amd as kda
+    S, H, V, K = 2, 2, 128, 128
+    print("case: int8 near half-integers S=%d H=%d V=%d K=%d" % (S, H, V, K), flush=True)
+    r = wl.rng(71)
+    amax = np.exp(r.uniform(-60.0, 60.0, size=(S, H, 1, K))).astype(np.float32)
+    amax[0, 0, 0, :8] = np.float32(1e-40) * np.arange(1, 9, dtype=np.float32)  # subnormal scales
+    amax[0, 1, 0, :8] = np.float32(127.0 * 2.0 ** -120) * (1 + np.arange(8, dtype=np.float32) / 64)
+    sc = (amax / np.float32(127.0)).astype(np.float32)
+    k = r.integers(-127, 127, size=(S, H, V, K)).astype(np.float32) + np.float32(0.5)
+    x = (k * sc).astype(np.float32)
+    nudge = r.integers(-3, 4, size=x.shape)
+    for step in range(1, 4):
+        up, dn = nudge >= step, nudge <= -step
+        x[up] = np.nextafter(x[up], np.float32(np.inf))
+        x[dn] = np.nextafter(x[dn], np.float32(-np.inf))
+    x = np.clip(x, -amax, amax)
+    x[:, :, 0, :] = amax[:, :, 0, :]     # row 0 carries the channel maximum
+    slots = 4
+    qd = torch.zeros((slots, H, V, K), dtype=torch.int8, device="cuda")
+    scd = torch.zeros((slots, H, 1, K), dtype=torch.float32, device="cuda")
+    idx = np.array([2, 0], dtype=np.int32)
+    kda.kda_ckpt_quantize_scatter(qd, scd, torch.from_numpy(idx).cuda(), torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    rq, rs = oracle.int8_quantize(x)
+    assert np.array_equal(qd[torch.from_numpy(idx.astype(np.int64)).cuda()].cpu().numpy(), rq)
+    assert np.array_equal(scd[torch.from_numpy(idx.astype(np.int64)).cuda()].cpu().numpy().view(np.uint32),
+                          rs.view(np.uint32))
 
 
 def test_prefill_resumes_from_int8_checkpoints():
