@@ -1435,20 +1435,21 @@ hipError_t launch_cfg(const Params& prm, bool bf16, hipStream_t stream) {
 }
 
 // Picks the kernel variant for these sizes and launches it.
-hipError_t launch_variant(Params prm, bool bf16, hipStream_t stream, bool wide = false) {
+hipError_t launch_variant(Params prm, bool bf16, hipStream_t stream) {
   const uintptr_t al = (uintptr_t)prm.q | (uintptr_t)prm.k | (uintptr_t)(prm.v_zero ? prm.k : prm.v) | (uintptr_t)prm.g;
   prm.pair = (prm.K % 2 == 0) && (prm.V % 2 == 0) && (al % 8 == 0);
   prm.ovec = (prm.V % 8 == 0) && ((uintptr_t)prm.out % 16 == 0);
   const uintptr_t sal = (prm.init_identity ? 0 : (uintptr_t)prm.init) | (uintptr_t)prm.fin | (uintptr_t)prm.ckpt;
   prm.svec = (prm.K % 4 == 0) && (sal % 16 == 0);
-  const int64_t chains = prm.N * prm.H;
-  // Few (sequence, head) chains: narrower value blocks give more workgroups.
   if (prm.K <= 64) {
     prm.nvb = (int)((prm.V + 63) / 64);
     return launch_cfg<64, 64>(prm, bf16, stream);
   }
-  // (wide: the segment passes size their chain count to one workgroup per CU)
-  if (prm.V <= 64 || (chains < 512 && !wide)) {
+  // 128-column value blocks whenever V allows, also for few (sequence, head)
+  // chains: 64-column blocks double the workgroups, but each repeats the
+  // key-side phases with half the waves, which costs more than the CUs it
+  // fills (1.2-2.2x slower from 8 to 480 chains of 2048-8192 tokens).
+  if (prm.V <= 64) {
     prm.nvb = (int)((prm.V + 63) / 64);
     return launch_cfg<128, 64>(prm, bf16, stream);
   }
@@ -1552,14 +1553,14 @@ hipError_t launch_chunk_prefill(const kda_prefill_args_t& a, hipStream_t stream)
     p1.ckpt = nullptr;
     p1.fin = bmap;
     p1.fin_bf16 = 0;
-    if ((e = launch_variant(p1, bf16, stream, true)) != hipSuccess) return e;
+    if ((e = launch_variant(p1, bf16, stream)) != hipSuccess) return e;
     // pass 1b: M of every segment (identity state, zero values, V = K)
     Params p2 = p1;
     p2.V = a.K;
     p2.v_zero = 1;
     p2.init_identity = 1;
     p2.fin = mmap;
-    if ((e = launch_variant(p2, bf16, stream, true)) != hipSuccess) return e;
+    if ((e = launch_variant(p2, bf16, stream)) != hipSuccess) return e;
     // scan: S_in of every segment, final states
     const int64_t ncb = (a.V + kScanCols - 1) / kScanCols;
     hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)(a.N * a.H * ncb)), dim3(256), 0, stream, sfirst, bmap, mmap,
@@ -1572,7 +1573,7 @@ hipError_t launch_chunk_prefill(const kda_prefill_args_t& a, hipStream_t stream)
     p3.fin = nullptr;
     p3.seq_of = sseq;
     p3.seq_cu = a.cu_seqlens;
-    return launch_variant(p3, bf16, stream, true);
+    return launch_variant(p3, bf16, stream);
   }
 
   if (a.N >= 2 && a.N <= kPlanMaxN) {

@@ -148,7 +148,7 @@ def test_bf16_ragged_varlen():
 
 
 def test_many_chains_take_full_value_blocks():
-    # N*H >= 512 selects the 128-wide value block
+    # 512 chains: twice as many workgroups as CUs
     inp = wl.host_prefill_inputs([40 + 3 * i for i in range(64)], 8, 128, 128, dtype="bf16", seed=6)
     _check(inp)
 
@@ -186,8 +186,9 @@ def test_single_token():
 @pytest.mark.parametrize("gval", [-30.0, -1e4])
 @pytest.mark.parametrize("lengths,H,K,V", [
     ([150, 70], 2, 64, 64),                            # K <= 64 kernel
-    ([150, 70], 2, 128, 128),                          # 64-column value blocks (few chains)
-    ([130 + 5 * (i % 7) for i in range(64)], 8, 128, 128),  # 128-column value blocks (>= 512 chains)
+    ([150, 70], 2, 128, 64),                           # 64-column value blocks (V <= 64)
+    ([150, 70], 2, 128, 128),                          # 128-column value blocks, few chains
+    ([130 + 5 * (i % 7) for i in range(64)], 8, 128, 128),  # 128-column value blocks, 512 chains
 ])
 def test_strong_decay_uses_shorter_chunks(gval, lengths, H, K, V):
     """Gate factors past 2^+-100 make a chunk retry as shorter chunks, after
