@@ -327,6 +327,12 @@ struct Params {
   // seq_cu the sequences' token offsets (NULL: items are whole sequences)
   const int32_t* seq_of;
   const int32_t* seq_cu;
+  // with seq_of: skip_last = 1 for the map passes (the last segment of each
+  // sequence is skipped: its map is never composed); otherwise the last
+  // segment of each sequence writes that sequence's final state (row seq_of[n]
+  // of fin), and only segments below *seg_total are real
+  int skip_last;
+  const int32_t* seg_total;
 };
 
 // Raw bits of one chunk's inputs as loaded (bf16 pairs packed in one word, a
@@ -424,6 +430,21 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
   const int64_t vcol = v0 + 16 * w + lr; // this lane's state column (state phase)
   const int64_t vcl = vcol < V ? vcol : V - 1;
   const int64_t srow = (n * H + h) * V;  // state row base of (n, h), in units of K elements
+  // final-state row and whether this item writes it (segments: see Params)
+  int64_t frow = srow;
+  bool fin_ok = true;
+  if (p.seq_of) {
+    const int64_t sq = p.seq_of[n];
+    int64_t se = p.seq_cu[sq + 1];
+    se = se < 0 ? 0 : (se > p.T ? p.T : se);
+    const bool last = eos == se;
+    if (p.skip_last) {
+      if (last) return;
+    } else {
+      fin_ok = last && n < (int64_t)*p.seg_total;
+      frow = (sq * H + h) * V;
+    }
+  }
 
   // A_qk upper blocks are read by the output product but never written: zero once.
   if constexpr (kOut) {
@@ -1231,20 +1252,26 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
   }
 
   // ---- final state ----
-  if (p.fin) store_state(S, p.fin, p.fin_bf16, p.svec, srow, lg, vcol, K, V);
+  if (p.fin && fin_ok) store_state(S, p.fin, p.fin_bf16, p.svec, frow, lg, vcol, K, V);
 }
 
 constexpr int64_t kPlanMaxN = 2048;
+constexpr int32_t kMinSplit = 3;  // fewest segments of the longest sequence worth the map passes
 
 // ---------------------------------------------------------------------------
 // Segment-parallel prefill of long sequences.  When a batch has too few
 // (sequence, head) chains to fill the GPU, every sequence is cut into
 // segments of seg_len tokens.  A segment acts on the state as an affine map
 // F(S) = M S + b (maps compose in order; the composition is associative):
-//   pass 1a: every segment from a zero state          -> b (its final state)
-//   pass 1b: every segment from the identity, with zero values -> M
-//   scan   : S_in(first) = initial, S_in(next) = M S_in + b, final state
-//   pass 2 : every segment again from its S_in        -> outputs
+//   pass 1a: every segment but the last of its sequence, from a zero state
+//            -> b (its final state)
+//   pass 1b: the same segments from the identity, with zero values -> M
+//   scan   : S_in(first) = initial, S_in(next) = M S_in + b
+//   pass 2 : every segment again from its S_in -> outputs; the last segment
+//            of each sequence writes the sequence's final state
+// When the longest sequence would get fewer than kMinSplit segments, every
+// sequence is one segment: passes 1a and 1b then have nothing to do and
+// pass 2 runs whole sequences.
 // All segments of all sequences run in parallel in passes 1 and 2.
 // ---------------------------------------------------------------------------
 
@@ -1260,16 +1287,22 @@ __global__ __launch_bounds__(1024) void seg_plan_kernel(const int32_t* __restric
     int64_t b0 = cu[n], e0 = cu[n + 1];
     b0 = b0 < 0 ? 0 : (b0 > T ? T : b0);
     e0 = e0 < b0 ? b0 : (e0 > T ? T : e0);
-    cnt[n] = (int32_t)((e0 - b0 + seg_len - 1) / seg_len);
+    const int64_t c = (e0 - b0 + seg_len - 1) / seg_len;
+    cnt[n] = (int32_t)(c > 1 ? c : 1);  // an empty sequence keeps one (empty) segment
   }
   __syncthreads();
   if (threadIdx.x == 0) {
+    // Whole sequences when the longest would get fewer than kMinSplit
+    // segments: the map passes then cost more than the parallelism returns.
+    int32_t cmax = 0;
+    for (int64_t n = 0; n < N; ++n) cmax = cnt[n] > cmax ? cnt[n] : cmax;
     // prefix sums, clamped to nmax so that offsets that break the cu_seqlens
     // precondition still cannot index past the workspace
     int64_t run = 0;
     for (int64_t n = 0; n < N; ++n) {
+      const int64_t c = cmax < kMinSplit ? 1 : cnt[n];
       first[n] = (int32_t)run;
-      run = run + cnt[n] < nmax ? run + cnt[n] : nmax;
+      run = run + c < nmax ? run + c : nmax;
     }
     first[N] = (int32_t)run;
   }
@@ -1293,8 +1326,9 @@ __global__ __launch_bounds__(1024) void seg_plan_kernel(const int32_t* __restric
 // Composes the segment maps of one (sequence, head) in fp32, for one block
 // of kScanCols value columns (the columns of S evolve independently under
 // S <- M S + b); 256 threads, K, V <= 128.  Writes each segment's initial
-// state S_in ([nmax, H, V, K] fp32) and the sequence's final state for these
-// columns.
+// state S_in ([nmax, H, V, K] fp32) for these columns.  The last segment of a
+// sequence has no map (its pass-2 run writes the final state), so the
+// composition stops before it.
 //
 // The map of a segment is stored as the state that pass 1b propagated from
 // the identity: row x of the [K][K] tile holds M's column x, so
@@ -1310,8 +1344,8 @@ constexpr int kScanV4 = 128 * 128 / 4 / kScanT;  // float4 of a 128 x 128 tile p
 
 __global__ __launch_bounds__(kScanT) void seg_scan_kernel(const int32_t* __restrict__ sfirst, const float* __restrict__ bmap,
                                                           const float* __restrict__ mmap, const void* __restrict__ init,
-                                                          int init_bf16, void* __restrict__ fin, int fin_bf16,
-                                                          float* __restrict__ sin, int64_t H, int64_t K, int64_t V) {
+                                                          int init_bf16, float* __restrict__ sin, int64_t H, int64_t K,
+                                                          int64_t V) {
   __shared__ __attribute__((aligned(16))) float sS[128 * kScanSL];  // S[c][v - v0]
   __shared__ __attribute__((aligned(16))) float sT[128 * kScanML];  // T[x][c]
   const int64_t ncb = (V + kScanCols - 1) / kScanCols;
@@ -1352,7 +1386,7 @@ __global__ __launch_bounds__(kScanT) void seg_scan_kernel(const int32_t* __restr
       br[j] = (r < K && v < V) ? bmap[((sg * H + h) * V + v) * K + r] : 0.f;
     }
   };
-  if (s0 < s1) fetch(s0);
+  if (s0 + 1 < s1) fetch(s0);
   __syncthreads();
   for (int64_t sg = s0; sg < s1; ++sg) {
     const int64_t srow_s = (sg * H + h) * V;
@@ -1360,6 +1394,7 @@ __global__ __launch_bounds__(kScanT) void seg_scan_kernel(const int32_t* __restr
       const int c = e & 127, vl = e >> 7;
       if (v0 + vl < V && c < K) sin[(srow_s + v0 + vl) * K + c] = sS[c * kScanSL + vl];
     }
+    if (sg + 1 == s1) break;  // uniform: the last segment's map is not composed
     if (vec) {
       const int q4 = (int)(K / 4);  // float4 per row
 #pragma unroll
@@ -1381,7 +1416,7 @@ __global__ __launch_bounds__(kScanT) void seg_scan_kernel(const int32_t* __restr
 #pragma unroll
     for (int j = 0; j < kScanCols / 2; ++j) acc[j] = br[j];
     __syncthreads();
-    if (sg + 1 < s1) fetch(sg + 1);  // lands while the product below runs
+    if (sg + 2 < s1) fetch(sg + 1);  // lands while the product below runs
     if (r < K) {
       for (int x = 0; x < K; ++x) {
         const float m = sT[x * kScanML + r];
@@ -1398,18 +1433,6 @@ __global__ __launch_bounds__(kScanT) void seg_scan_kernel(const int32_t* __restr
 #pragma unroll
     for (int j = 0; j < kScanCols / 2; ++j) sS[r * kScanSL + j0 + j] = acc[j];
     __syncthreads();
-  }
-  if (fin) {
-    for (int e = tid; e < kScanCols * 128; e += kScanT) {
-      const int c = e & 127, vl = e >> 7;
-      if (c < K && v0 + vl < V) {
-        const int64_t o = (srow + v0 + vl) * K + c;
-        if (fin_bf16)
-          static_cast<__bf16*>(fin)[o] = (__bf16)sS[c * kScanSL + vl];
-        else
-          static_cast<float*>(fin)[o] = sS[c * kScanSL + vl];
-      }
-    }
   }
 }
 
@@ -1528,6 +1551,8 @@ hipError_t launch_chunk_prefill(const kda_prefill_args_t& a, hipStream_t stream)
   prm.ckpt_bf16 = a.ckpt_dtype == KDA_BF16;
   prm.seq_of = nullptr;
   prm.seq_cu = nullptr;
+  prm.skip_last = 0;
+  prm.seg_total = nullptr;
   const bool bf16 = a.qkv_dtype == KDA_BF16;
   hipError_t e;
 
@@ -1553,6 +1578,9 @@ hipError_t launch_chunk_prefill(const kda_prefill_args_t& a, hipStream_t stream)
     p1.ckpt = nullptr;
     p1.fin = bmap;
     p1.fin_bf16 = 0;
+    p1.seq_of = sseq;
+    p1.seq_cu = a.cu_seqlens;
+    p1.skip_last = 1;
     if ((e = launch_variant(p1, bf16, stream)) != hipSuccess) return e;
     // pass 1b: M of every segment (identity state, zero values, V = K)
     Params p2 = p1;
@@ -1564,15 +1592,15 @@ hipError_t launch_chunk_prefill(const kda_prefill_args_t& a, hipStream_t stream)
     // scan: S_in of every segment, final states
     const int64_t ncb = (a.V + kScanCols - 1) / kScanCols;
     hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)(a.N * a.H * ncb)), dim3(256), 0, stream, sfirst, bmap, mmap,
-                       a.initial_state, prm.init_bf16, a.final_state, prm.fin_bf16, sin, a.H, a.K, a.V);
+                       a.initial_state, prm.init_bf16, sin, a.H, a.K, a.V);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // pass 2: outputs of every segment from its true initial state
     Params p3 = seg;
     p3.init = sin;
     p3.init_bf16 = 0;
-    p3.fin = nullptr;
     p3.seq_of = sseq;
     p3.seq_cu = a.cu_seqlens;
+    p3.seg_total = sfirst + a.N;
     return launch_variant(p3, bf16, stream);
   }
 

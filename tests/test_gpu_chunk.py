@@ -244,6 +244,8 @@ def test_deterministic():
     ([17000, 100, 0], 4, 128, 128, "bf16", True),
     ([9000, 9001], 3, 32, 48, "f32", True),
     ([17000], 2, 30, 50, "bf16", True),   # K not a multiple of 4: element loads in the map scan
+    ([4096] * 4, 2, 128, 128, "bf16", True),         # at most two segments each: whole sequences
+    ([4096, 0, 4096, 4096, 4096], 2, 64, 64, "f32", True),  # whole sequences and an empty one
 ])
 def test_segmented_long_sequences(lengths, H, K, V, dtype, init):
     import kda_recurrent_state_amd as kda
