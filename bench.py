@@ -10,7 +10,10 @@ flags, unique scatter targets.  Inputs are resident in HBM before timing.
 
 Prints ONE JSON line: whole-step tokens/s, per-stage kernel times from HIP
 events on the launch stream, the chunk kernel's HBM roofline fraction, copy
-bandwidths and the oracle timed on the host's cores on a bounded sample.
+bandwidths, the other configurations of the metric under "configs" (state
+copy with int32 and int64 indices, varlen and long prefill, each with its own
+roofline), and the oracle timed on the host's cores on bounded samples (all
+threads and one thread; scalar gather/scatter at one and all threads).
 """
 from __future__ import annotations
 
@@ -118,15 +121,29 @@ def build_workload(seed: int, device):
     packed_in = torch.empty((MAX_SELECTED, H, V, K), dtype=torch.bfloat16, device=device)
     packed_out = torch.empty((MAX_SELECTED, H, V, K), dtype=torch.bfloat16, device=device)
     out = torch.empty_like(inp["v"])
-    ws = torch.empty(max(256, 4 * N), dtype=torch.uint8, device=device)
+    import kda_recurrent_state_amd as kda
+    ws_bytes = max(1, kda.kda_chunk_prefill_workspace_size(inp["T"], N, H, K, V))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
     return dict(inp=inp, cache=cache, backing=back, N=N, lengths=lengths,
                 gidx=torch.from_numpy(gidx).to(device), flags=torch.from_numpy(flags).to(device),
                 sidx=torch.from_numpy(sidx).to(device), gidx_np=gidx, flags_np=flags, sidx_np=sidx,
                 packed_in=packed_in, packed_out=packed_out, out=out, ws=ws)
 
 
-def cpu_baseline(seed: int, budget_s: float):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
+def cpu_baseline(seed: int, budget_s: float, single_budget_s: float = 8.0, copy_budget_s: float = 6.0):
+    """The oracle, as it stands, on bounded samples of the same workloads.
+
+    * recurrence, all threads (``value``): the fp64 token recurrence with
+      OpenMP over (sequence, head) chains on the first sequences of the e2e
+      batch, sized to ``budget_s`` after a calibration run;
+    * recurrence, one thread: the same on fewer sequences;
+    * scalar gather / scatter GB/s at one thread and at all threads: the
+      oracle's element-by-element copy on the copy workload's row format
+      (fp32 rows [32,128,128] = 2 MiB, 4096-element gaps), the selection
+      split into contiguous parts, one per thread.
+    """
+    import concurrent.futures as cf
+
     import kda_workloads as wl
     import oracle
 
@@ -134,28 +151,71 @@ def cpu_baseline(seed: int, budget_s: float):
     threads = oracle.default_threads()
     lengths = wl.lengths_e2e(seed)
 
-    def run(lens):
+    def run(lens, nthreads):
         inp = wl.host_prefill_inputs(lens, H, K, V, dtype="bf16", seed=seed + 11, initial=True, init_dtype="bf16")
         t0 = time.perf_counter()
         oracle.kda_recurrence(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["cu_seqlens"],
-                              inp["initial"], threads=threads)
+                              inp["initial"], threads=nthreads)
         return time.perf_counter() - t0
 
-    # calibrate on one short sequence, then size the sample to the budget
+    def sample_for(rate, budget):
+        target_tokens = max(64, int(rate * budget))
+        sample, tot = [], 0
+        for L in lengths:
+            if tot + L > target_tokens and sample:
+                break
+            sample.append(L)
+            tot += L
+        return sample
+
+    # calibrate on one short sequence, then size the samples to the budgets
     probe = [min(lengths)]
-    t_probe = run(probe)
-    rate = sum(probe) / max(t_probe, 1e-6)
-    target_tokens = max(64, int(rate * budget_s))
-    sample, tot = [], 0
-    for L in lengths:
-        if tot + L > target_tokens and sample:
-            break
-        sample.append(L)
-        tot += L
-    dt = run(sample)
+    rate1 = sum(probe) / max(run(probe, 1), 1e-6)   # one thread: all heads of one sequence
+    sample = sample_for(rate1 * min(threads, H), budget_s)
+    dt = run(sample, threads)
+    sample1 = sample_for(rate1, single_budget_s)
+    dt1 = run(sample1, 1)
+
+    # scalar copies: 64 rows of the copy workload's format, 32 selected
+    rows, S = 64, 32
+    backing, off, shape, strides = wl.host_cache(rows, H, V, K, dtype="f32", gap=wl.GAP, offset=1024, seed=seed)
+    gidx = wl.copy_indices(seed, S, rows, 2, "int32")
+    flags = wl.copy_flags(seed, S, 3)
+    sidx = wl.copy_indices(seed + 1, S, rows, 2, "int32", unique=True)
+    payload = H * V * K * 4
+    g_bytes = (int(((gidx >= 0) & (gidx < rows) & (flags != 0)).sum()) + S) * payload
+    s_bytes = 2 * int(((sidx >= 0) & (sidx < rows)).sum()) * payload
+    packed = oracle.state_gather(backing, off, shape, strides, gidx, flags)
+
+    def copy_rate(nthreads, what):
+        parts = [p for p in np.array_split(np.arange(S), nthreads) if len(p)]
+        def one(p):
+            if what == "gather":
+                oracle.state_gather(backing, off, shape, strides, gidx[p], flags[p])
+            else:
+                oracle.state_scatter(backing, off, shape, strides, sidx[p], packed[p], in_place=True)
+        reps, t_used = 0, 0.0
+        with cf.ThreadPoolExecutor(max_workers=len(parts)) as ex:
+            while reps == 0 or t_used < copy_budget_s / 4:
+                t0 = time.perf_counter()
+                list(ex.map(one, parts))
+                t_used += time.perf_counter() - t0
+                reps += 1
+        return reps * (g_bytes if what == "gather" else s_bytes) / t_used / 1e9
+
+    copy = {"gather_GBps_1_thread": copy_rate(1, "gather"), "gather_GBps_all_threads": copy_rate(threads, "gather"),
+            "scatter_GBps_1_thread": copy_rate(1, "scatter"),
+            "scatter_GBps_all_threads": copy_rate(threads, "scatter"),
+            "sample": "fp32 cache [%d,32,128,128] with row stride payload+4096, %d rows selected (2 invalid "
+                      "indices, 3 false flags in gather; unique targets in scatter), element-by-element raw-bit "
+                      "copy; algorithmic bytes as for the GPU copies" % (rows, S)}
     return {"value": sum(sample) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "first %d of the %d sequences (%d tokens, all %d heads, K=V=128), fp64 token recurrence, "
-                      "%.1f s" % (len(sample), len(lengths), sum(sample), H, dt)}
+            "sample": "first %d of the %d e2e sequences (%d tokens, all %d heads, K=V=128), fp64 token "
+                      "recurrence, %d threads, %.1f s" % (len(sample), len(lengths), sum(sample), H, threads, dt),
+            "single_thread": {"value": sum(sample1) / dt1, "unit": "tokens/s", "cores": 1,
+                              "sample": "first %d e2e sequences (%d tokens, all %d heads), %.1f s"
+                                        % (len(sample1), sum(sample1), H, dt1)},
+            "copy": copy}
 
 
 def calibrate_copy(device, gib: float = 1.0):
@@ -188,43 +248,140 @@ def _timed(fn, steps, warmup):
     return wall * 1e3 / steps, float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
 
+def measure_copy(dev, seed: int, steps: int, warmup: int):
+    """State copy workload: fp32 cache [1024,32,128,128] with row stride
+    payload+4096 at a storage offset, S=256 gathered (with replacement) and
+    scattered (unique targets), 13 invalid indices, 26 false flags; int32 and
+    int64 indices.  GB/s = algorithmic bytes / average event time of a call."""
+    import torch
+    import kda_recurrent_state_amd as kda
+    import kda_workloads as wl
+    nrows, S = 1024, 256
+    back, off, shape, strides = wl.device_cache(nrows, H, V, K, dtype="f32", gap=wl.GAP, offset=1024,
+                                                seed=seed, device=dev)
+    cache = torch.as_strided(back.view(torch.float32), shape, strides, off)
+    packed = torch.empty((S, H, V, K), dtype=torch.float32, device=dev)
+    payload = H * V * K * 4
+    res = {}
+    for it in ("int32", "int64"):
+        gidx = wl.copy_indices(seed, S, nrows, 13, it, unique=False, huge=True)
+        flags = wl.copy_flags(seed, S, 26)
+        sidx = wl.copy_indices(seed + 1, S, nrows, 13, it, unique=True, huge=True)
+        gi, fl, si = (torch.from_numpy(x).to(dev) for x in (gidx, flags, sidx))
+        n_read = int(((gidx >= 0) & (gidx < nrows) & (flags != 0)).sum())
+        n_valid = int(((sidx >= 0) & (sidx < nrows)).sum())
+        g_bytes, s_bytes = (n_read + S) * payload, 2 * n_valid * payload
+        _, g_ms = _timed(lambda: kda.kda_state_gather(cache, gi, fl, packed), steps, warmup)
+        _, s_ms = _timed(lambda: kda.kda_state_scatter(cache, si, packed), steps, warmup)
+        g_gbps, s_gbps = g_bytes / (g_ms * 1e-3) / 1e9, s_bytes / (s_ms * 1e-3) / 1e9
+        res[it] = {"gather_GBps": g_gbps, "scatter_GBps": s_gbps, "gather_ms": g_ms, "scatter_ms": s_ms,
+                   "gather_bytes": g_bytes, "scatter_bytes": s_bytes,
+                   "gather_frac_hbm": g_gbps / HBM_PEAK_GBPS, "scatter_frac_hbm": s_gbps / HBM_PEAK_GBPS}
+    del back, cache, packed
+    torch.cuda.synchronize()
+    worst = min(min(r["gather_GBps"], r["scatter_GBps"]) for r in res.values())
+    avg = float(np.mean([x for r in res.values() for x in (r["gather_GBps"], r["scatter_GBps"])]))
+    return {"value": avg, "unit": "GB/s", "dtype": "f32",
+            "workload": "state copy: fp32 cache [1024,32,128,128], row stride payload+4096, S=256, 13 invalid "
+                        "indices, 26 false flags, int32 and int64 indices",
+            "roofline": {"bound": "hbm", "achieved": avg, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": avg / HBM_PEAK_GBPS, "traffic": None, "kernel": "state_copy_kernel",
+                         "worst_call_frac": worst / HBM_PEAK_GBPS},
+            "per_index_type": res, "steps": steps, "warmup": warmup}
+
+
+def measure_chunk(dev, seed: int, steps: int, warmup: int, which: str):
+    """Chunk prefill on the varlen workload (16 sequences of U[512,4096]
+    tokens, fp32 initial and final states) or the long one (one 65536-token
+    sequence; initial state gathered from a bf16 cache row, final state
+    scattered back as bf16).  The roofline is that of the kda_chunk_prefill
+    call: its algorithmic bytes / its average event time (for the long
+    sequence the call is the segment-parallel chain of kernels)."""
+    import torch
+    import kda_recurrent_state_amd as kda
+    import kda_workloads as wl
+    stream = torch.cuda.current_stream()
+    if which == "varlen":
+        lengths = wl.lengths_varlen(seed)
+        inp = wl.device_prefill_inputs(lengths, H, K, V, dtype="bf16", seed=seed, device=dev, init_dtype="f32")
+        state_bytes = 4
+        desc = "varlen chunk prefill: 16 sequences, lengths U[512,4096], H=32, K=V=128, fp32 initial/final states"
+    else:
+        lengths = wl.lengths_long()
+        inp = wl.device_prefill_inputs(lengths, H, K, V, dtype="bf16", seed=seed, device=dev, initial=False)
+        state_bytes = 2
+        desc = ("long prefill: one 65536-token sequence, H=32, K=V=128, state gathered from / scattered to "
+                "bf16 cache rows [4,32,128,128] (row gap 4096)")
+    T, N = inp["T"], inp["N"]
+    out = torch.empty_like(inp["v"])
+    fin = torch.empty((N, H, V, K), dtype=torch.float32 if which == "varlen" else torch.bfloat16, device=dev)
+    ws = torch.empty(max(1, kda.kda_chunk_prefill_workspace_size(T, N, H, K, V)), dtype=torch.uint8, device=dev)
+    if which == "long":
+        back, off, shape, strides = wl.device_cache(4, H, V, K, dtype="bf16", gap=wl.GAP, offset=0,
+                                                    seed=seed + 1, device=dev)
+        cache = torch.as_strided(back.view(torch.bfloat16), shape, strides, off)
+        gi = torch.tensor([1], dtype=torch.int32, device=dev)
+        si = torch.tensor([3], dtype=torch.int32, device=dev)
+        fl = torch.ones(1, dtype=torch.uint8, device=dev)
+        init = torch.empty((1, H, V, K), dtype=torch.bfloat16, device=dev)
+    else:
+        init = inp["initial"]
+
+    def step(ev=None):
+        if which == "long":
+            kda.kda_state_gather(cache, gi, fl, init)
+        if ev is not None:
+            ev[0].record(stream)
+        kda.kda_chunk_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["cu_seqlens"],
+                              initial_state=init, out=out, final_state=fin, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+        if which == "long":
+            kda.kda_state_scatter(cache, si, fin)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    ms_wall = (time.perf_counter() - t0) * 1e3 / steps
+    c_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    c_avg = float(np.mean(c_ms))
+    nbytes = T * H * (2 * K + 2 * K + 2 * V + 4 * K + 4 + 2 * V) + N * H * 2 * K * V * state_bytes + 4 * (N + 1)
+    achieved = nbytes / (c_avg * 1e-3) / 1e9
+    return {"value": T / (c_avg * 1e-3), "unit": "tokens/s", "dtype": "bf16", "workload": desc,
+            "tokens": T, "sequences": N, "seed": seed, "ms_per_step": ms_wall, "chunk_prefill_ms": c_avg,
+            "chunk_prefill_percentiles_ms": pct(c_ms),
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "kda_chunk_prefill",
+                         "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": c_avg},
+            "steps": steps, "warmup": warmup}
+
+
 def bench_other(args, dev):
-    """Secondary workloads (not the headline line): varlen, long, copy."""
+    """Secondary workloads (their own line, not the headline): copy, varlen,
+    long, int8, decode."""
     import torch
     import kda_recurrent_state_amd as kda
     import kda_workloads as wl
     base = {"metric": METRIC, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
     if args.workload == "copy":
-        nrows = 1024
-        back, off, shape, strides = wl.device_cache(nrows, H, V, K, dtype="f32", gap=wl.GAP, offset=1024,
-                                                    seed=args.seed, device=dev)
-        cache = torch.as_strided(back.view(torch.float32), shape, strides, off)
-        S = 256
-        res = {}
-        for it in ("int32", "int64"):
-            gidx = wl.copy_indices(args.seed, S, nrows, 13, it, unique=False, huge=True)
-            flags = wl.copy_flags(args.seed, S, 26)
-            sidx = wl.copy_indices(args.seed + 1, S, nrows, 13, it, unique=True, huge=True)
-            gi, fl, si = (torch.from_numpy(x).to(dev) for x in (gidx, flags, sidx))
-            packed = torch.empty((S, H, V, K), dtype=torch.float32, device=dev)
-            payload = H * V * K * 4
-            n_read = int(((gidx >= 0) & (gidx < nrows) & (flags != 0)).sum())
-            n_valid = int(((sidx >= 0) & (sidx < nrows)).sum())
-            _, g_ms = _timed(lambda: kda.kda_state_gather(cache, gi, fl, packed), args.steps, args.warmup)
-            _, s_ms = _timed(lambda: kda.kda_state_scatter(cache, si, packed), args.steps, args.warmup)
-            res[it] = {"gather_GBps": (n_read + S) * payload / (g_ms * 1e-3) / 1e9,
-                       "scatter_GBps": 2 * n_valid * payload / (s_ms * 1e-3) / 1e9, "gather_ms": g_ms, "scatter_ms": s_ms}
-        gb = float(np.mean([r["gather_GBps"] for r in res.values()]))
-        sb = float(np.mean([r["scatter_GBps"] for r in res.values()]))
-        base.update({"metric": "state gather/scatter GB/s, 1 GPU", "unit": "GB/s", "value": (gb + sb) / 2,
+        m = measure_copy(dev, args.seed, args.steps, args.warmup)
+        base.update({"metric": "state gather/scatter GB/s, 1 GPU", "unit": "GB/s", "value": m["value"],
                      "dtype": "f32", "ms_per_step": None,
-                     "config": {"workload": "state copy: fp32 cache [1024,32,128,128], row stride payload+4096, "
-                                            "S=256, 13 invalid indices, 26 false flags", "seq_len": None},
-                     "roofline": {"bound": "hbm", "achieved": (gb + sb) / 2, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                                  "frac": (gb + sb) / 2 / HBM_PEAK_GBPS, "traffic": None,
-                                  "kernel": "state_copy_kernel"},
-                     "per_index_type": res})
+                     "config": {"workload": m["workload"], "seq_len": None, "seed": args.seed},
+                     "roofline": m["roofline"], "per_index_type": m["per_index_type"]})
+        return base
+    if args.workload in ("varlen", "long"):
+        m = measure_chunk(dev, args.seed, args.steps, args.warmup, args.workload)
+        base.update({"value": m["value"], "ms_per_step": m["ms_per_step"],
+                     "config": {"workload": m["workload"], "tokens": m["tokens"], "global_batch": m["sequences"],
+                                "seq_len": m["tokens"], "seed": args.seed},
+                     "roofline": m["roofline"], "chunk_prefill_percentiles_ms": m["chunk_prefill_percentiles_ms"]})
         return base
     if args.workload == "int8":
         slots, S = 1024, 256
@@ -281,47 +438,7 @@ def bench_other(args, dev):
                                   "kernel": "recurrent_decode_kernel",
                                   "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": ms_ev}})
         return base
-    if args.workload == "varlen":
-        lengths = wl.lengths_varlen(args.seed)
-        inp = wl.device_prefill_inputs(lengths, H, K, V, dtype="bf16", seed=args.seed, device=dev, init_dtype="f32")
-        T, N = inp["T"], inp["N"]
-        out = torch.empty_like(inp["v"])
-        fin = torch.empty((N, H, V, K), dtype=torch.float32, device=dev)
-        ws = torch.empty(4096, dtype=torch.uint8, device=dev)
-        fn = lambda: kda.kda_chunk_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],  # noqa: E731
-                                           inp["cu_seqlens"], initial_state=inp["initial"], out=out,
-                                           final_state=fin, workspace=ws)
-        nbytes = T * H * (2 * K + 2 * K + 2 * V + 4 * K + 4 + 2 * V) + N * H * 2 * K * V * 4
-        desc = "varlen chunk prefill: 16 sequences, lengths U[512,4096], H=32, K=V=128, fp32 states"
-    else:
-        lengths = wl.lengths_long()
-        inp = wl.device_prefill_inputs(lengths, H, K, V, dtype="bf16", seed=args.seed, device=dev, initial=False)
-        T, N = inp["T"], inp["N"]
-        back, off, shape, strides = wl.device_cache(4, H, V, K, dtype="bf16", gap=wl.GAP, offset=0,
-                                                    seed=args.seed + 1, device=dev)
-        cache = torch.as_strided(back.view(torch.bfloat16), shape, strides, off)
-        gi = torch.tensor([1], dtype=torch.int32, device=dev)
-        si = torch.tensor([3], dtype=torch.int32, device=dev)
-        fl = torch.ones(1, dtype=torch.uint8, device=dev)
-        pin = torch.empty((1, H, V, K), dtype=torch.bfloat16, device=dev)
-        pout = torch.empty_like(pin)
-        out = torch.empty_like(inp["v"])
-
-        def fn():
-            kda.kda_state_gather(cache, gi, fl, pin)
-            kda.kda_chunk_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["cu_seqlens"],
-                                  initial_state=pin, out=out, final_state=pout)
-            kda.kda_state_scatter(cache, si, pout)
-        nbytes = T * H * (2 * K + 2 * K + 2 * V + 4 * K + 4 + 2 * V) + N * H * 2 * K * V * 2
-        desc = "long prefill: one 65536-token sequence, H=32, K=V=128, state gathered from / scattered to bf16 cache rows"
-    ms_wall, ms_ev = _timed(fn, args.steps, args.warmup)
-    base.update({"value": T / (ms_wall * 1e-3), "ms_per_step": ms_wall,
-                 "config": {"workload": desc, "tokens": T, "global_batch": N, "seq_len": T, "seed": args.seed},
-                 "roofline": {"bound": "hbm", "achieved": nbytes / (ms_ev * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
-                              "unit": "GB/s", "frac": nbytes / (ms_ev * 1e-3) / 1e9 / HBM_PEAK_GBPS, "traffic": None,
-                              "kernel": "kda_chunk_prefill" + (" (+ copies)" if args.workload == "long" else ""),
-                              "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": ms_ev}})
-    return base
+    raise ValueError(args.workload)
 
 
 def bench_ckpt(args, dev, interval: int = 1024):
@@ -394,8 +511,13 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=41)
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of multi-threaded oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sub-steps", type=int, default=20,
+                    help="timed steps of each other configuration carried in the headline line (copy, varlen, long)")
+    ap.add_argument("--no-sub-configs", action="store_true",
+                    help="leave the copy / varlen / long configurations out of the headline line")
     ap.add_argument("--calibrate-copy", action="store_true", help="run only a plain 1 GiB device copy")
     ap.add_argument("--workload", default="e2e", choices=["e2e", "varlen", "long", "copy", "ckpt", "decode", "int8"],
                     help="e2e (default, the headline step); varlen / long: the chunk prefill on 16 sequences of "
@@ -484,6 +606,15 @@ def main():
     t_hbm, t_mfma = chunk_bytes / (HBM_PEAK_GBPS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
     t_roof = max(t_hbm, t_mfma)
 
+    # the other configurations of the metric, each with its own roofline:
+    # copy (fp32 rows, int32 and int64 indices), varlen and long prefill
+    subs = None
+    if not args.no_sub_configs:
+        sw = min(3, args.warmup)
+        subs = {"copy": measure_copy(dev, args.seed, args.sub_steps, sw),
+                "varlen": measure_chunk(dev, args.seed, args.sub_steps, sw, "varlen"),
+                "long": measure_chunk(dev, args.seed, args.sub_steps, sw, "long")}
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.seed, args.cpu_budget)
@@ -511,6 +642,7 @@ def main():
                      "kernel": "kda_chunk_prefill", "algorithmic_bytes_per_launch": chunk_bytes,
                      "avg_launch_ms": c_avg},
         "cpu_baseline": cpu,
+        "configs": subs,
         "stages_ms": {"gather": g_avg, "chunk_prefill": c_avg, "scatter": s_avg},
         "copy_GBps": {"gather": gather_bytes / (g_avg * 1e-3) / 1e9,
                       "scatter": scatter_bytes / (s_avg * 1e-3) / 1e9,

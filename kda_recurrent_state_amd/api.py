@@ -31,6 +31,21 @@ def _stream_handle(stream, device) -> int:
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _on_stream(stream, device, *tensors) -> None:
+    """Tensors this binding allocated on the current stream but that a kernel
+    uses on another ``stream``: tell PyTorch's caching allocator, so their
+    memory is not handed out again before that stream's work is done."""
+    if stream is None:
+        return
+    if not hasattr(stream, "cuda_stream"):
+        stream = torch.cuda.ExternalStream(int(stream), device=device)
+    if stream.cuda_stream == torch.cuda.current_stream(device).cuda_stream:
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
 def _device(*ts) -> torch.device:
     """The one device that all given tensors live on (device tensors only)."""
     dev = None
@@ -77,6 +92,7 @@ def kda_state_gather(cache: torch.Tensor, indices: torch.Tensor, flags: Optional
     S = indices.shape[0]
     if packed is None:
         packed = torch.empty((S,) + tuple(cache.shape[1:]), dtype=cache.dtype, device=cache.device)
+        _on_stream(stream, dev, packed)
     if packed.dtype != cache.dtype or not packed.is_contiguous() or tuple(packed.shape) != (S,) + tuple(cache.shape[1:]):
         raise KDAError("kda_state_gather", 3, "packed must be a contiguous [S,H,V,K] tensor of the cache dtype")
     fptr = None
@@ -149,12 +165,15 @@ def kda_chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torc
         raise KDAError("kda_chunk_prefill", 3, "beta must be [T,H]")
     if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or N < 0:
         raise KDAError("kda_chunk_prefill", 2, "cu_seqlens must be int32 [N+1]")
+    made = []   # tensors allocated here (on the current stream)
     if out is None:
         out = torch.empty((T, H, V), dtype=q.dtype, device=q.device)
+        made.append(out)
     if out.dtype != q.dtype or tuple(out.shape) != (T, H, V) or not out.is_contiguous():
         raise KDAError("kda_chunk_prefill", 3, "out must be a contiguous [T,H,V] tensor of q's dtype")
     if final_state is None and final_dtype is not None and N > 0:
         final_state = torch.empty((N, H, V, K), dtype=final_dtype, device=q.device)
+        made.append(final_state)
     for name, s in (("initial_state", initial_state), ("final_state", final_state)):
         if s is not None and (tuple(s.shape) != (N, H, V, K) or not s.is_contiguous()):
             raise KDAError("kda_chunk_prefill", 3, "%s must be a contiguous [N,H,V,K] tensor" % name)
@@ -164,8 +183,13 @@ def kda_chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torc
         if ckpt_states.dim() != 4 or tuple(ckpt_states.shape[1:]) != (H, V, K) or not ckpt_states.is_contiguous():
             raise KDAError("kda_chunk_prefill", 3, "ckpt_states must be a contiguous [num_ckpt,H,V,K] tensor")
     need = int(lib.kda_chunk_prefill_workspace_size(T, N, H, K, V))
-    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+    if need > 0 and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        made.append(workspace)
+    if need > 0 and workspace.numel() * workspace.element_size() < need:
+        raise KDAError("kda_chunk_prefill", 7, "workspace of %d bytes, need %d (kda_chunk_prefill_workspace_size)"
+                       % (workspace.numel() * workspace.element_size(), need))
+    _on_stream(stream, dev, *made)
     a = PrefillArgs()
     a.T, a.N, a.H, a.K, a.V = T, N, H, K, V
     a.q, a.k, a.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
@@ -224,6 +248,7 @@ def kda_recurrent_decode(cache: torch.Tensor, state_indices: torch.Tensor, q: to
         raise KDAError("kda_recurrent_decode", 3, "state_indices must be [N]")
     if out is None:
         out = torch.empty((N, H, V), dtype=q.dtype, device=q.device)
+        _on_stream(stream, dev, out)
     if out.dtype != q.dtype or tuple(out.shape) != (N, H, V) or not out.is_contiguous():
         raise KDAError("kda_recurrent_decode", 3, "out must be a contiguous [N,H,V] tensor of q's dtype")
     d = cache_descriptor(cache)
@@ -292,6 +317,7 @@ def kda_ckpt_dequantize_gather(qdata: torch.Tensor, scale: torch.Tensor, indices
     S = int(indices.shape[0])
     if packed is None:
         packed = torch.empty((S,) + tuple(qdata.shape[1:]), dtype=dtype, device=qdata.device)
+        _on_stream(stream, dev, packed)
     if tuple(packed.shape) != (S,) + tuple(qdata.shape[1:]) or not packed.is_contiguous():
         raise KDAError("kda_ckpt_dequantize_gather", 3, "packed must be a contiguous [S,H,V,K] tensor")
     fptr = None

@@ -111,10 +111,17 @@ def state_gather(backing: np.ndarray, offset: int, shape, strides, indices: np.n
 
 
 def state_scatter(backing: np.ndarray, offset: int, shape, strides, indices: np.ndarray,
-                  packed: np.ndarray) -> np.ndarray:
-    """Return a copy of ``backing`` with the valid packed rows written to the cache view."""
+                  packed: np.ndarray, in_place: bool = False) -> np.ndarray:
+    """Return a copy of ``backing`` with the valid packed rows written to the
+    cache view (``in_place``: write into ``backing`` itself, which must be a
+    contiguous array, and return it)."""
     lib = _load()
-    out = np.array(backing, copy=True)
+    if in_place:
+        if not backing.flags.c_contiguous:
+            raise ValueError("in-place scatter needs a contiguous backing array")
+        out = backing
+    else:
+        out = np.array(backing, copy=True)
     eb = out.dtype.itemsize
     nrows, H, V, K = (int(x) for x in shape)
     st = np.asarray(strides, dtype=np.int64)
