@@ -218,6 +218,37 @@ size_t kda_chunk_prefill_workspace_size(int64_t T, int64_t N, int64_t H, int64_t
 kda_status_t kda_chunk_prefill(const kda_prefill_args_t* args, void* stream);
 
 /*
+ * Bytes of device scratch that kda_chunk_prefill_noalloc keeps on each device
+ * it runs on: 96 MiB, more than kda_chunk_prefill_workspace_size returns for
+ * any sizes kda_chunk_prefill accepts.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+
+/*
+ * kda_chunk_prefill_noalloc -- kda_chunk_prefill for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, semantics, validation and
+ * kernels as kda_chunk_prefill, except that args->workspace and
+ * args->workspace_bytes are ignored: the workspace is a static device array of
+ * KDA_NOALLOC_SCRATCH_BYTES inside the library, one copy per device, created
+ * when the library's code is loaded on that device and held until the process
+ * ends.  The call allocates and frees nothing (no hipMalloc, no hipFree, no
+ * allocating library routine) and enqueues no memset.  The first call on a
+ * device looks up that device's copy (hipGetSymbolAddress) with the device
+ * current.
+ * Calls on one device share that device's array: two calls that can overlap
+ * in time on one device (different streams, or different host threads with
+ * no ordering between them) race on it and give undefined results; order
+ * them on one stream or with events.  Calls on different devices do not
+ * interact.  Nothing is carried from one call to the next.
+ * Errors: as kda_chunk_prefill, with KDA_E_WORKSPACE when
+ * kda_chunk_prefill_workspace_size(T, N, H, K, V) exceeds
+ * KDA_NOALLOC_SCRATCH_BYTES (no accepted size does), and KDA_E_HIP if the
+ * scratch array cannot be located on the current device.
+ */
+kda_status_t kda_chunk_prefill_noalloc(const kda_prefill_args_t* args, void* stream);
+
+/*
  * Arguments of kda_recurrent_decode: one new token for each of N sequences.
  * All pointers are device pointers to contiguous row-major arrays.
  *  N, H, K, V      -- sequences (= tokens), heads, key dim (1..128), value dim (>= 1);

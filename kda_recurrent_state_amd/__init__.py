@@ -16,10 +16,12 @@ is no fallback implementation.
 """
 from ._lib import KDAError, load_library  # noqa: F401
 from .api import (KDAStateCopy, cache_descriptor, checkpoint_offsets, int8_store_descriptor,  # noqa: F401
-                  kda_chunk_prefill, kda_chunk_prefill_workspace_size, kda_ckpt_dequantize_gather,
+                  kda_chunk_prefill, kda_chunk_prefill_noalloc, kda_chunk_prefill_workspace_size,
+                  kda_ckpt_dequantize_gather,
                   kda_ckpt_quantize_scatter, kda_recurrent_decode, kda_state_gather, kda_state_scatter)
 
 __all__ = ["kda_state_gather", "kda_state_scatter", "kda_chunk_prefill", "kda_chunk_prefill_workspace_size",
+           "kda_chunk_prefill_noalloc",
            "kda_recurrent_decode", "kda_ckpt_quantize_scatter", "kda_ckpt_dequantize_gather",
            "int8_store_descriptor",
            "KDAStateCopy", "KDAError", "load_library", "cache_descriptor", "checkpoint_offsets"]

@@ -14,6 +14,7 @@ STATUS_NAMES = {0: "KDA_OK", 1: "KDA_E_NULL", 2: "KDA_E_DTYPE", 3: "KDA_E_SHAPE"
                 5: "KDA_E_OVERLAP", 6: "KDA_E_UNSUPPORTED", 7: "KDA_E_WORKSPACE", 8: "KDA_E_ALIAS",
                 9: "KDA_E_HIP"}
 EXPORTED = ("kda_state_gather", "kda_state_scatter", "kda_chunk_prefill", "kda_chunk_prefill_workspace_size",
+            "kda_chunk_prefill_noalloc",
             "kda_recurrent_decode", "kda_ckpt_quantize_scatter", "kda_ckpt_dequantize_gather",
             "kda_status_string", "kda_last_error_detail")
 
@@ -81,6 +82,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_state_scatter.restype = ctypes.c_int
     lib.kda_chunk_prefill.argtypes = [ctypes.POINTER(PrefillArgs), vp]
     lib.kda_chunk_prefill.restype = ctypes.c_int
+    lib.kda_chunk_prefill_noalloc.argtypes = [ctypes.POINTER(PrefillArgs), vp]
+    lib.kda_chunk_prefill_noalloc.restype = ctypes.c_int
     lib.kda_recurrent_decode.argtypes = [ctypes.POINTER(StateCache), ctypes.POINTER(DecodeArgs), vp]
     lib.kda_recurrent_decode.restype = ctypes.c_int
     lib.kda_ckpt_quantize_scatter.argtypes = [ctypes.POINTER(Int8Store), vp, ctypes.c_int, i64, vp, ctypes.c_int, vp]

@@ -147,47 +147,70 @@ def kda_chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torc
     row ckpt_cu[n]+j receives the state of sequence n after
     (j+1)*ckpt_interval tokens; ckpt_interval is a positive multiple of 64.
     """
+    return _prefill("kda_chunk_prefill", q, k, v, g, beta, cu_seqlens, initial_state, out, final_state,
+                    final_dtype, scale, use_qk_l2norm, workspace, stream, ckpt_interval, ckpt_cu, ckpt_states)
+
+
+def kda_chunk_prefill_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                              beta: torch.Tensor, cu_seqlens: torch.Tensor, out: torch.Tensor,
+                              initial_state: Optional[torch.Tensor] = None,
+                              final_state: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                              use_qk_l2norm: bool = True, stream=None, ckpt_interval: int = 0,
+                              ckpt_cu: Optional[torch.Tensor] = None, ckpt_states: Optional[torch.Tensor] = None):
+    """kda_chunk_prefill that allocates nothing: ``out`` (and ``final_state``,
+    if wanted) are the caller's, and the workspace is the library's static
+    per-device scratch.  Calls that can overlap on one device race on that
+    scratch.  Returns (out, final_state)."""
+    return _prefill("kda_chunk_prefill_noalloc", q, k, v, g, beta, cu_seqlens, initial_state, out, final_state,
+                    None, scale, use_qk_l2norm, None, stream, ckpt_interval, ckpt_cu, ckpt_states)
+
+
+def _prefill(entry, q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, final_dtype, scale,
+             use_qk_l2norm, workspace, stream, ckpt_interval, ckpt_cu, ckpt_states):
+    noalloc = entry == "kda_chunk_prefill_noalloc"
     lib = _lib.load_library()
     dev = _device(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, workspace, ckpt_cu, ckpt_states)
     if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
-        raise KDAError("kda_chunk_prefill", 3, "q,k must be [T,H,K] and v [T,H,V]")
+        raise KDAError(entry, 3, "q,k must be [T,H,K] and v [T,H,V]")
     T, H, K = (int(x) for x in q.shape)
     V = int(v.shape[2])
     N = int(cu_seqlens.numel()) - 1
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("cu_seqlens", cu_seqlens)):
         if not t.is_contiguous():
-            raise KDAError("kda_chunk_prefill", 4, "%s must be contiguous" % name)
+            raise KDAError(entry, 4, "%s must be contiguous" % name)
     if k.dtype != q.dtype or v.dtype != q.dtype:
-        raise KDAError("kda_chunk_prefill", 2, "q, k, v must share a dtype")
+        raise KDAError(entry, 2, "q, k, v must share a dtype")
     if g.dtype != torch.float32 or tuple(g.shape) != (T, H, K):
-        raise KDAError("kda_chunk_prefill", 2, "g must be float32 [T,H,K]")
+        raise KDAError(entry, 2, "g must be float32 [T,H,K]")
     if tuple(beta.shape) != (T, H):
-        raise KDAError("kda_chunk_prefill", 3, "beta must be [T,H]")
+        raise KDAError(entry, 3, "beta must be [T,H]")
     if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or N < 0:
-        raise KDAError("kda_chunk_prefill", 2, "cu_seqlens must be int32 [N+1]")
+        raise KDAError(entry, 2, "cu_seqlens must be int32 [N+1]")
+    if noalloc and out is None:
+        raise KDAError(entry, 1, "out must be given (the call allocates nothing)")
     made = []   # tensors allocated here (on the current stream)
     if out is None:
         out = torch.empty((T, H, V), dtype=q.dtype, device=q.device)
         made.append(out)
     if out.dtype != q.dtype or tuple(out.shape) != (T, H, V) or not out.is_contiguous():
-        raise KDAError("kda_chunk_prefill", 3, "out must be a contiguous [T,H,V] tensor of q's dtype")
+        raise KDAError(entry, 3, "out must be a contiguous [T,H,V] tensor of q's dtype")
     if final_state is None and final_dtype is not None and N > 0:
         final_state = torch.empty((N, H, V, K), dtype=final_dtype, device=q.device)
         made.append(final_state)
     for name, s in (("initial_state", initial_state), ("final_state", final_state)):
         if s is not None and (tuple(s.shape) != (N, H, V, K) or not s.is_contiguous()):
-            raise KDAError("kda_chunk_prefill", 3, "%s must be a contiguous [N,H,V,K] tensor" % name)
+            raise KDAError(entry, 3, "%s must be a contiguous [N,H,V,K] tensor" % name)
     if ckpt_states is not None:
         if ckpt_cu is None or ckpt_cu.dtype != torch.int32 or ckpt_cu.numel() != N + 1:
-            raise KDAError("kda_chunk_prefill", 2, "ckpt_cu must be int32 [N+1]")
+            raise KDAError(entry, 2, "ckpt_cu must be int32 [N+1]")
         if ckpt_states.dim() != 4 or tuple(ckpt_states.shape[1:]) != (H, V, K) or not ckpt_states.is_contiguous():
-            raise KDAError("kda_chunk_prefill", 3, "ckpt_states must be a contiguous [num_ckpt,H,V,K] tensor")
-    need = int(lib.kda_chunk_prefill_workspace_size(T, N, H, K, V))
+            raise KDAError(entry, 3, "ckpt_states must be a contiguous [num_ckpt,H,V,K] tensor")
+    need = 0 if noalloc else int(lib.kda_chunk_prefill_workspace_size(T, N, H, K, V))
     if need > 0 and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         made.append(workspace)
     if need > 0 and workspace.numel() * workspace.element_size() < need:
-        raise KDAError("kda_chunk_prefill", 7, "workspace of %d bytes, need %d (kda_chunk_prefill_workspace_size)"
+        raise KDAError(entry, 7, "workspace of %d bytes, need %d (kda_chunk_prefill_workspace_size)"
                        % (workspace.numel() * workspace.element_size(), need))
     _on_stream(stream, dev, *made)
     a = PrefillArgs()
@@ -214,8 +237,8 @@ def kda_chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torc
         a.num_ckpt = int(ckpt_states.shape[0])
         a.ckpt_dtype = _dtype_code(ckpt_states, "kda_chunk_prefill")
     with torch.cuda.device(dev):
-        st = lib.kda_chunk_prefill(ctypes.byref(a), _stream_handle(stream, dev))
-    _lib.check("kda_chunk_prefill", st)
+        st = getattr(lib, entry)(ctypes.byref(a), _stream_handle(stream, dev))
+    _lib.check(entry, st)
     return out, final_state
 
 

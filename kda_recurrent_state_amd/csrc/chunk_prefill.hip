@@ -51,6 +51,7 @@
 //    shared q/k/g tiles are served from one L2.
 #include "internal.h"
 
+#include <mutex>
 #include <type_traits>
 
 namespace kda {
@@ -1611,6 +1612,39 @@ hipError_t launch_chunk_prefill(const kda_prefill_args_t& a, hipStream_t stream)
     prm.order = order;
   }
   return launch_variant(prm, bf16, stream);
+}
+
+}  // namespace kda
+
+// Scratch of the allocation-free entry point (kda_chunk_prefill_noalloc): the
+// workspace of the sequence-order plan and of the segment maps, one copy per
+// device, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: its device address on the current
+// device comes from hipGetSymbolAddress, and only that address is handed to
+// kernels.  Nothing in it needs to start at zero (every kernel that reads a
+// part of it reads only what an earlier kernel of the same call wrote).
+static __device__ __align__(256) char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+namespace kda {
+
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace kda

@@ -32,4 +32,8 @@ hipError_t launch_int8_ckpt(bool quantize, const kda_int8_store_t& store, const 
 // Workspace bytes launch_chunk_prefill uses for these sizes.
 size_t chunk_prefill_workspace_bytes(int64_t T, int64_t N, int64_t H, int64_t K, int64_t V);
 
+// Device address of the current device's copy of the library's static
+// scratch array (KDA_NOALLOC_SCRATCH_BYTES bytes), looked up once per device.
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace kda

@@ -161,7 +161,15 @@ size_t kda_chunk_prefill_workspace_size(int64_t T, int64_t N, int64_t H, int64_t
   return kda::chunk_prefill_workspace_bytes(T, N, H, K, V);
 }
 
-kda_status_t kda_chunk_prefill(const kda_prefill_args_t* a, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by kda_chunk_prefill and kda_chunk_prefill_noalloc: every
+// check but the caller's workspace.  *need receives the workspace bytes the
+// call uses; KDA_OK with a->N == 0 means there is nothing to enqueue.
+kda_status_t check_prefill(const kda_prefill_args_t* a, size_t* need) {
+  *need = 0;
   if (!a) return KDA_E_NULL;
   if (a->T < 0 || a->N < 0 || a->H <= 0 || a->K <= 0 || a->V <= 0) return KDA_E_SHAPE;
   if (a->N == 0 && a->T != 0) return KDA_E_SHAPE;
@@ -181,7 +189,7 @@ kda_status_t kda_chunk_prefill(const kda_prefill_args_t* a, void* stream) {
   if (a->N == 0) return KDA_OK;
   if (!a->cu_seqlens) return KDA_E_NULL;
   if (a->T > 0 && (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->out)) return KDA_E_NULL;
-  const size_t need = kda::chunk_prefill_workspace_bytes(a->T, a->N, a->H, a->K, a->V);
+  *need = kda::chunk_prefill_workspace_bytes(a->T, a->N, a->H, a->K, a->V);
   {
     // out may be exactly v and final_state exactly initial_state (same
     // dtype); any other overlap between an output and an argument is an error
@@ -199,13 +207,47 @@ kda_status_t kda_chunk_prefill(const kda_prefill_args_t* a, void* stream) {
     const Span outs[4] = {{a->out, TH * a->V * eb},
                           {a->final_state, a->final_state ? NHVK * dtype_bytes(a->final_dtype) : 0},
                           {a->ckpt_states, a->ckpt_states ? a->num_ckpt * a->H * a->V * a->K * dtype_bytes(a->ckpt_dtype) : 0},
-                          {need > 0 ? a->workspace : nullptr, (int64_t)need}};
+                          {*need > 0 ? a->workspace : nullptr, (int64_t)*need}};
     const int same[4] = {2, 6, -1, -1};
     if (alias_error(outs, same, 4, ins, 8)) return KDA_E_ALIAS;
   }
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_chunk_prefill(const kda_prefill_args_t* a, void* stream) {
+  size_t need = 0;
+  const kda_status_t st = check_prefill(a, &need);
+  if (st != KDA_OK || a->N == 0) return st;
   if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return KDA_E_WORKSPACE;
   hipError_t e = kda::launch_chunk_prefill(*a, static_cast<hipStream_t>(stream));
   return hip_status("kda_chunk_prefill launch", e);
+}
+
+kda_status_t kda_chunk_prefill_noalloc(const kda_prefill_args_t* a, void* stream) {
+  kda_prefill_args_t b;
+  size_t need = 0;
+  if (a) {
+    // the caller's workspace fields play no part
+    b = *a;
+    b.workspace = nullptr;
+    b.workspace_bytes = 0;
+  }
+  const kda_status_t st = check_prefill(a ? &b : nullptr, &need);
+  if (st != KDA_OK || b.N == 0) return st;
+  if (need > KDA_NOALLOC_SCRATCH_BYTES) return KDA_E_WORKSPACE;
+  if (need > 0) {
+    // this device's copy of the library's scratch array (set up on the first
+    // call on each device)
+    hipError_t e = kda::noalloc_scratch(&b.workspace);
+    if (e != hipSuccess) return hip_status("kda_chunk_prefill_noalloc scratch lookup", e);
+    b.workspace_bytes = KDA_NOALLOC_SCRATCH_BYTES;
+  }
+  hipError_t e = kda::launch_chunk_prefill(b, static_cast<hipStream_t>(stream));
+  return hip_status("kda_chunk_prefill_noalloc launch", e);
 }
 
 kda_status_t kda_recurrent_decode(const kda_state_cache_t* cache, const kda_decode_args_t* a, void* stream) {

@@ -311,3 +311,51 @@ def test_binding_refuses_without_library(tmp_path):
             _lib.load_library(str(tmp_path / "missing.so"))
     finally:
         _lib._lib = saved
+
+
+def _noalloc_max():
+    with open(os.path.join(ROOT, "include", "kda.h")) as f:
+        m = re.search(r"#define KDA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", f.read())
+    return int(m.group(1)) << int(m.group(2))
+
+
+def test_noalloc_scratch_covers_every_accepted_size(lib):
+    """The static scratch of kda_chunk_prefill_noalloc holds the workspace of
+    every size kda_chunk_prefill accepts.  The segment maps are the largest
+    part: with N*H < 256 chains the segment length is at least T*H/256, so a
+    batch has at most N*H + 256 (segment, head) maps of 3*K*V*4 bytes
+    (K, V <= 128 on that path) -- at most 511 * 192 KiB; the sequence-order
+    plan needs 4 bytes per sequence for N <= 2048."""
+    import numpy as np
+    mx = _noalloc_max()
+    assert 511 * 3 * 128 * 128 * 4 + 64 * 1024 <= mx
+    ts = sorted(set([int(x) for x in np.geomspace(16384, 1 << 26, 300)] + [2048 * k for k in range(8, 520)]))
+    worst = 0
+    for H in range(1, 256):
+        for N in sorted({1, 2, 3, max(1, 255 // H), max(1, 255 // H // 2)}):
+            if N * H >= 256:
+                continue
+            for T in ts:
+                worst = max(worst, lib.kda_chunk_prefill_workspace_size(T, N, H, 128, 128))
+    for N in (2, 100, 2048, 2049, 5000):
+        worst = max(worst, lib.kda_chunk_prefill_workspace_size(10 ** 6, N, 32, 128, 128))
+    assert 0 < worst <= mx, (worst, mx)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=129), 6), (dict(qkv_dtype=3), 2), (dict(q=0), 1), (dict(out=0x1000), 8),
+])
+def test_noalloc_rejections(lib, kw, status):
+    # the same validation as kda_chunk_prefill, before any HIP call
+    a = _args(**kw)
+    assert lib.kda_chunk_prefill_noalloc(ctypes.byref(a), None) == status
+
+
+def test_noalloc_ignores_the_workspace_fields(lib):
+    # N = 4 needs a workspace; the allocation-free call takes it from its own
+    # scratch, so a missing caller workspace is no error -- checked here with
+    # an argument that fails afterwards (NULL cu_seqlens), before any HIP call
+    a = _args(N=4, workspace=0, workspace_bytes=0, cu_seqlens=0)
+    assert lib.kda_chunk_prefill_noalloc(ctypes.byref(a), None) == 1
+    assert lib.kda_chunk_prefill_noalloc(None, None) == 1
+    assert lib.kda_chunk_prefill_noalloc(ctypes.byref(_args(N=0, T=0)), None) == 0
