@@ -315,8 +315,11 @@ struct Params {
   int pair;              // K, V even and q/k/v/g 8-byte aligned: two channels per load
   int ovec;              // V % 8 == 0 and out 16-byte aligned: 16-byte output stores
   int svec;              // K % 4 == 0 and state pointers aligned: vector state I/O
-  int v_zero;            // values are all zero (v is not read)
-  int init_identity;     // initial state is the identity (K == V); init is not read
+  // segment maps (kOut = false): fin receives b = F(0) and mmap receives M
+  // (the state propagated from the identity with zero values, rows [seg, H,
+  // K, K]: row x of a (segment, head) tile is M's column x), written by the
+  // first value block of each (segment, head)
+  float* mmap;
   // chunk-boundary checkpoints: the state after every ckpt_iv tokens of a
   // sequence goes to row ckpt_cu[seq] + j of ckpt (rows outside [0, num_ckpt)
   // are skipped)
@@ -381,8 +384,12 @@ __device__ __forceinline__ void store_state(const f32x4 (&S)[KT], void* dst, int
   }
 }
 
-// kOut = false: maps of segments only (out == NULL); q, the query tiles, A_qk
-// and the output products are not computed.
+// kOut = false: affine maps F(S) = M S + b of segments (out == NULL): from a
+// zero state with the chunk's values (-> b) and, in the same pass, from the
+// identity with zero values (-> M, propagated through the same W, Kbar and
+// decays; its U is zero); q, the query tiles, A_qk and the output products
+// are not computed.  Launched with BV == KP so that the K columns of M are
+// one 16-column tile per wave.
 template <int KP, int BV, bool kBF16, bool kOut>
 __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
   using C = Cfg<KP, BV>;
@@ -457,12 +464,18 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
 
   // ---- initial state, MFMA C layout: S[ct][e] = S(c = 16ct + 4lg + e, vcol) ----
   f32x4 S[C::KT];
-  if (p.init_identity) {
+  // maps: M's column mcol of this lane, from the identity (first value block only)
+  const int mcol = 16 * w + lr;
+  const bool map_m = !kOut && vb == 0 && p.mmap;  // uniform
+  f32x4 SM[kOut ? 1 : C::KT];
+  if constexpr (!kOut) {
+    static_assert(kOut || BV == KP, "maps run with BV == KP");
 #pragma unroll
     for (int ct = 0; ct < C::KT; ++ct)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) S[ct][e] = (16 * ct + 4 * lg + e == vcol && vcol < V) ? 1.f : 0.f;
-  } else if (p.init) {
+      for (int e = 0; e < 4; ++e) SM[ct][e] = (16 * ct + 4 * lg + e == mcol && mcol < K) ? 1.f : 0.f;
+  }
+  if (p.init) {
     if (p.svec) {
 #pragma unroll
       for (int ct = 0; ct < C::KT; ++ct) {
@@ -506,42 +519,40 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
   // or the key/value range are zeroed in phase 0.
   using Raw = RawChunk<RPW, CPL, VPL, kBF16>;
   Raw raw;
-  // (with zero values v is never dereferenced: loads of v read k's rows instead)
-  const void* const vsrc = p.v_zero ? p.k : p.v;
-  const int64_t vstride = p.v_zero ? K : V;
-  auto issue_loads = [&](int64_t tb) {
+  const void* const vsrc = p.v;
+  const int64_t vstride = V;
+  // Loads of rows RPW*w + r, r in [r0, r1), of the chunk starting at tb (r0
+  // and r1 are constants at every call, so the loop unrolls to the rows
+  // asked for): rows past the span re-read its last row, channels past K and
+  // columns past V re-read the last valid one.
+  auto issue_rows = [&](int64_t tb, int r0, int r1) __attribute__((always_inline)) {
     const int64_t span = (len - tb) < (int64_t)kC ? (len - tb) : (int64_t)kC;
     if (p.pair) {
-      // Uniform 64-bit bases at the chunk's first (token, head) row and
-      // 32-bit offsets from them (H * max(K, V) <= 2^22 keeps a chunk's
-      // offsets below 2^31 bytes); two key channels (CPL == 2) / value
-      // columns (VPL == 2) per access.
-      constexpr uint32_t eb = kBF16 ? 2 : 4;
-      const int64_t row0 = (bos + tb) * H + h;
-      const char* kb = static_cast<const char*>(p.k) + row0 * K * eb;
-      const char* qb = static_cast<const char*>(p.q) + row0 * K * eb;
-      const char* vb = static_cast<const char*>(vsrc) + row0 * vstride * eb;
-      const char* gb = reinterpret_cast<const char*>(p.g) + row0 * K * 4;
-      const char* bb = static_cast<const char*>(p.beta) + row0 * (p.beta_bf16 ? 2 : 4);
-      const uint32_t cs = (uint32_t)(CPL == 2 ? (c_lo + 1 < K ? c_lo : K - 2) : (c_lo < K ? c_lo : K - 1));
-      const uint32_t vs = (uint32_t)(VPL == 2 ? (vc_lo + 1 < V ? vc_lo : V - 2) : (vc_lo < V ? vc_lo : V - 1));
-      uint32_t ri[RPW];  // (token, head) rows after row0, clamped to the span
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
+        if (r < r0 || r >= r1) continue;
         const int i = RPW * w + r;
-        ri[r] = (uint32_t)((i < span ? i : span - 1) * H);
-      }
-      if (p.beta_bf16) {
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) raw.b[r] = ld_at<unsigned short>(bb, 2 * ri[r]);
-      } else {
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) raw.b[r] = ld_at<unsigned>(bb, 4 * ri[r]);
-      }
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        const uint32_t ek = ri[r] * (uint32_t)K + cs;        // element offset in k, q, g
-        const uint32_t ev = ri[r] * (uint32_t)vstride + vs;  // element offset in v
+        const int64_t ir = i < span ? i : span - 1;
+        // Uniform 64-bit bases at the chunk's first (token, head) row and
+        // 32-bit offsets from them (H * max(K, V) <= 2^22 keeps a chunk's
+        // offsets below 2^31 bytes); two key channels (CPL == 2) / value
+        // columns (VPL == 2) per access.
+        constexpr uint32_t eb = kBF16 ? 2 : 4;
+        const int64_t row0 = (bos + tb) * H + h;
+        const char* kb = static_cast<const char*>(p.k) + row0 * K * eb;
+        const char* qb = static_cast<const char*>(p.q) + row0 * K * eb;
+        const char* vb = static_cast<const char*>(vsrc) + row0 * vstride * eb;
+        const char* gb = reinterpret_cast<const char*>(p.g) + row0 * K * 4;
+        const char* bb = static_cast<const char*>(p.beta) + row0 * (p.beta_bf16 ? 2 : 4);
+        const uint32_t cs = (uint32_t)(CPL == 2 ? (c_lo + 1 < K ? c_lo : K - 2) : (c_lo < K ? c_lo : K - 1));
+        const uint32_t vs = (uint32_t)(VPL == 2 ? (vc_lo + 1 < V ? vc_lo : V - 2) : (vc_lo < V ? vc_lo : V - 1));
+        const uint32_t ri = (uint32_t)(ir * H);  // (token, head) rows after row0
+        if (p.beta_bf16)
+          raw.b[r] = ld_at<unsigned short>(bb, 2 * ri);
+        else
+          raw.b[r] = ld_at<unsigned>(bb, 4 * ri);
+        const uint32_t ek = ri * (uint32_t)K + cs;        // element offset in k, q, g
+        const uint32_t ev = ri * (uint32_t)vstride + vs;  // element offset in v
         if (kBF16) {
           if (CPL == 2) {
             raw.k[r][0] = ld_at<unsigned>(kb, 2 * ek);
@@ -576,38 +587,31 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
         }
       }
     } else {
-      int64_t th[RPW];
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        const int i = RPW * w + r;
-        th[r] = (bos + tb + (i < span ? i : span - 1)) * H + h;
-      }
-      if (p.beta_bf16) {
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) raw.b[r] = static_cast<const unsigned short*>(p.beta)[th[r]];
-      } else {
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) raw.b[r] = static_cast<const unsigned*>(p.beta)[th[r]];
-      }
       // element by element (odd K or V, or unaligned tensors); bf16 pairs are
       // packed after the loads return
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
+        if (r < r0 || r >= r1) continue;
+        const int i = RPW * w + r;
+        const int64_t ir = i < span ? i : span - 1;
+        const int64_t th = (bos + tb + ir) * H + h;
+        raw.b[r] = p.beta_bf16 ? (unsigned)static_cast<const unsigned short*>(p.beta)[th]
+                               : static_cast<const unsigned*>(p.beta)[th];
         unsigned kk[CPL], qq[CPL], vv2[VPL];
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) {
           const int64_t cs = c_lo + cc < K ? c_lo + cc : K - 1;
-          kk[cc] = kBF16 ? (unsigned)static_cast<const unsigned short*>(p.k)[th[r] * K + cs]
-                         : static_cast<const unsigned*>(p.k)[th[r] * K + cs];
-          qq[cc] = kBF16 ? (unsigned)static_cast<const unsigned short*>(p.q)[th[r] * K + cs]
-                         : static_cast<const unsigned*>(p.q)[th[r] * K + cs];
-          raw.g[r][cc] = p.g[th[r] * K + cs];
+          kk[cc] = kBF16 ? (unsigned)static_cast<const unsigned short*>(p.k)[th * K + cs]
+                         : static_cast<const unsigned*>(p.k)[th * K + cs];
+          qq[cc] = kBF16 ? (unsigned)static_cast<const unsigned short*>(p.q)[th * K + cs]
+                         : static_cast<const unsigned*>(p.q)[th * K + cs];
+          raw.g[r][cc] = p.g[th * K + cs];
         }
 #pragma unroll
         for (int vv = 0; vv < VPL; ++vv) {
           const int64_t vs = vc_lo + vv < V ? vc_lo + vv : V - 1;
-          vv2[vv] = kBF16 ? (unsigned)static_cast<const unsigned short*>(vsrc)[th[r] * vstride + vs]
-                          : static_cast<const unsigned*>(vsrc)[th[r] * vstride + vs];
+          vv2[vv] = kBF16 ? (unsigned)static_cast<const unsigned short*>(vsrc)[th * vstride + vs]
+                          : static_cast<const unsigned*>(vsrc)[th * vstride + vs];
         }
         if (kBF16 && CPL == 2) {
           raw.k[r][0] = kk[0] | (kk[CPL - 1] << 16);
@@ -628,6 +632,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
       }
     }
   };
+  auto issue_loads = [&](int64_t tb) __attribute__((always_inline)) { issue_rows(tb, 0, RPW); };
 
   // Checkpoints: ck_next is the next checkpoint position relative to bos and
   // ck_row its row (both uniform).  Chunks never straddle a multiple of 64
@@ -679,7 +684,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     // loaded clamped: zero their bits before anything is unpacked (a full
     // chunk has none; uniform branch).  Masking the loaded words in place
     // keeps a single unpack path after the branch.
-    if (!(L == kC && K == KP && v0 + BV <= V && !p.v_zero)) {
+    if (!(L == kC && K == KP && v0 + BV <= V)) {
       unsigned mk[Raw::KW], mv[Raw::VW];  // this lane's channel / column masks per word
 #pragma unroll
       for (int cw = 0; cw < Raw::KW; ++cw) {
@@ -691,9 +696,9 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
 #pragma unroll
       for (int vw = 0; vw < Raw::VW; ++vw) {
         if (kBF16 && VPL == 2)
-          mv[vw] = p.v_zero ? 0u : ((vc_lo < V ? 0xffffu : 0u) | (vc_lo + 1 < V ? 0xffff0000u : 0u));
+          mv[vw] = (vc_lo < V ? 0xffffu : 0u) | (vc_lo + 1 < V ? 0xffff0000u : 0u);
         else
-          mv[vw] = (!p.v_zero && vc_lo + vw < V) ? ~0u : 0u;
+          mv[vw] = vc_lo + vw < V ? ~0u : 0u;
       }
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
@@ -1112,20 +1117,10 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     // V_new = U - W S, O = Qg S + A_qk V_new, S = D S + Kbar^T V_new.  Each
     // product reads its LDS operands ahead of the MFMAs that use them, so the
     // read latency overlaps the MFMAs already issued.
-    bf16x8 bS[C::KS];
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) bS[ks] = pack_perm(S[2 * ks], S[2 * ks + 1]);
-    // 2^gamma_L of this lane's state rows, read now so that the reads overlap V_new
-    f32x4 dec[C::KT];
-#pragma unroll
-    for (int ct = 0; ct < C::KT; ++ct) dec[ct] = *reinterpret_cast<const f32x4*>(sDec + 16 * ct + 4 * lg);
-    // V_new: contraction step outer, row tile inner (the four accumulators
-    // advance together, so consecutive MFMAs are independent); the next
-    // step's four operands are read before this step's MFMAs
-    f32x4 Vn[4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) Vn[rt] = U[rt];
-    {
+    // Vn -= W St: contraction step outer, row tile inner (the four
+    // accumulators advance together, so consecutive MFMAs are independent);
+    // the next step's four operands are read before this step's MFMAs
+    auto sub_w_product = [&](const bf16x8 (&bSt)[C::KS], f32x4 (&Vn)[4]) __attribute__((always_inline)) {
       bf16x8 a[2][4];
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) a[0][rt] = ld8(sW + (16 * rt + lr) * C::LDK + 8 * lg);
@@ -1137,9 +1132,39 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
             a[(ks + 1) & 1][rt] = ld8(sW + (16 * rt + lr) * C::LDK + 32 * (ks + 1) + 8 * lg);
         }
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) Vn[rt] = mfma(a[ks & 1][rt], bS[ks], Vn[rt]);
+        for (int rt = 0; rt < 4; ++rt) Vn[rt] = mfma(a[ks & 1][rt], bSt[ks], Vn[rt]);
       }
-    }
+    };
+    // St += Kbar^T V_new: a ring of four Kbar^T operands in flight
+    auto add_kbar_product = [&](f32x4 (&St)[C::KT], const bf16x8 (&bV)[2]) __attribute__((always_inline)) {
+      constexpr int NU = 2 * C::KT;  // (q2, ct) steps, q2 outer
+      // 16-byte run 4 q2 + lg of row 16 ct + lr (kb_pos; the swizzle depends on lr only)
+      const int kb0 = lr * kC + 8 * (lg ^ ((lr >> 1) & 7)), kb1 = lr * kC + 8 * ((4 + lg) ^ ((lr >> 1) & 7));
+      bf16x8 kr[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        kr[t] = ld8(sKB + 16 * kC * (t % C::KT) + (t / C::KT ? kb1 : kb0));
+#pragma unroll
+      for (int t = 0; t < NU; ++t) {
+        const int q2 = t / C::KT, ct = t % C::KT;
+        St[ct] = mfma(kr[t & 3], bV[q2], St[ct]);
+        if (t + 4 < NU) {
+          const int q2n = (t + 4) / C::KT, ctn = (t + 4) % C::KT;
+          kr[t & 3] = ld8(sKB + 16 * kC * ctn + (q2n ? kb1 : kb0));
+        }
+      }
+    };
+    // 2^gamma_L of this lane's state rows, read now so that the reads overlap V_new
+    f32x4 dec[C::KT];
+#pragma unroll
+    for (int ct = 0; ct < C::KT; ++ct) dec[ct] = *reinterpret_cast<const f32x4*>(sDec + 16 * ct + 4 * lg);
+    bf16x8 bS[C::KS];
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) bS[ks] = pack_perm(S[2 * ks], S[2 * ks + 1]);
+    f32x4 Vn[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) Vn[rt] = U[rt];
+    sub_w_product(bS, Vn);
     bf16x8 bV[2];
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) bV[q2] = pack_perm(Vn[2 * q2], Vn[2 * q2 + 1]);
@@ -1178,23 +1203,25 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
         O[rt] = mfma(bV[q2], aq[t], O[rt]);
       }
     }
-    // S update: a ring of four Kbar^T operands in flight
-    {
-      constexpr int NU = 2 * C::KT;  // (q2, ct) steps, q2 outer
-      // 16-byte run 4 q2 + lg of row 16 ct + lr (kb_pos; the swizzle depends on lr only)
-      const int kb0 = lr * kC + 8 * (lg ^ ((lr >> 1) & 7)), kb1 = lr * kC + 8 * ((4 + lg) ^ ((lr >> 1) & 7));
-      bf16x8 kr[4];
+    add_kbar_product(S, bV);
+    if constexpr (!kOut) {
+      // segment maps, M part (after the b part, whose U and V_new are then
+      // dead): V_new = -W S_M (zero values), S_M = D S_M + Kbar^T V_new
+      if (map_m) {
+        __builtin_amdgcn_sched_barrier(0);  // the b part's registers are free before the M part starts
+        bf16x8 bM[C::KS];
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        kr[t] = ld8(sKB + 16 * kC * (t % C::KT) + (t / C::KT ? kb1 : kb0));
+        for (int ks = 0; ks < C::KS; ++ks) bM[ks] = pack_perm(SM[2 * ks], SM[2 * ks + 1]);
+        f32x4 Vm[4];
 #pragma unroll
-      for (int t = 0; t < NU; ++t) {
-        const int q2 = t / C::KT, ct = t % C::KT;
-        S[ct] = mfma(kr[t & 3], bV[q2], S[ct]);
-        if (t + 4 < NU) {
-          const int q2n = (t + 4) / C::KT, ctn = (t + 4) % C::KT;
-          kr[t & 3] = ld8(sKB + 16 * kC * ctn + (q2n ? kb1 : kb0));
-        }
+        for (int rt = 0; rt < 4; ++rt) Vm[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sub_w_product(bM, Vm);
+        bf16x8 bVm[2];
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) bVm[q2] = pack_perm(Vm[2 * q2], Vm[2 * q2 + 1]);
+#pragma unroll
+        for (int ct = 0; ct < C::KT; ++ct) SM[ct] *= *reinterpret_cast<const f32x4*>(sDec + 16 * ct + 4 * lg);
+        add_kbar_product(SM, bVm);
       }
     }
 
@@ -1254,6 +1281,9 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
 
   // ---- final state ----
   if (p.fin && fin_ok) store_state(S, p.fin, p.fin_bf16, p.svec, frow, lg, vcol, K, V);
+  if constexpr (!kOut) {
+    if (map_m) store_state(SM, p.mmap, 0, p.svec, (n * H + h) * K, lg, (int64_t)mcol, K, K);
+  }
 }
 
 constexpr int64_t kPlanMaxN = 2048;
@@ -1264,15 +1294,15 @@ constexpr int32_t kMinSplit = 3;  // fewest segments of the longest sequence wor
 // (sequence, head) chains to fill the GPU, every sequence is cut into
 // segments of seg_len tokens.  A segment acts on the state as an affine map
 // F(S) = M S + b (maps compose in order; the composition is associative):
-//   pass 1a: every segment but the last of its sequence, from a zero state
-//            -> b (its final state)
-//   pass 1b: the same segments from the identity, with zero values -> M
+//   pass 1 : every segment but the last of its sequence, in one pass: from a
+//            zero state -> b (its final state), and from the identity with
+//            zero values -> M (the same chunk operators act on both)
 //   scan   : S_in(first) = initial, S_in(next) = M S_in + b
 //   pass 2 : every segment again from its S_in -> outputs; the last segment
 //            of each sequence writes the sequence's final state
 // When the longest sequence would get fewer than kMinSplit segments, every
-// sequence is one segment: passes 1a and 1b then have nothing to do and
-// pass 2 runs whole sequences.
+// sequence is one segment: pass 1 then has nothing to do and pass 2 runs
+// whole sequences.
 // All segments of all sequences run in parallel in passes 1 and 2.
 // ---------------------------------------------------------------------------
 
@@ -1331,7 +1361,7 @@ __global__ __launch_bounds__(1024) void seg_plan_kernel(const int32_t* __restric
 // sequence has no map (its pass-2 run writes the final state), so the
 // composition stops before it.
 //
-// The map of a segment is stored as the state that pass 1b propagated from
+// The map of a segment is stored as the state that pass 1 propagated from
 // the identity: row x of the [K][K] tile holds M's column x, so
 // S_new[r] = b[r] + sum_x T[x][r] S[x].  T is kept in LDS as stored (thread
 // r reads column r: consecutive addresses across lanes) and the next
@@ -1444,30 +1474,36 @@ hipError_t launch_cfg(const Params& prm, bool bf16, hipStream_t stream) {
   const int64_t grid = groups * 8 * prm.nvb;
   constexpr int nt = Cfg<KP, BV>::NT;
   const dim3 g3((unsigned)grid), b3(nt);
-  if (prm.out) {
-    if (bf16)
-      hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, true, true>), g3, b3, 0, stream, prm);
-    else
-      hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, false, true>), g3, b3, 0, stream, prm);
-  } else {
-    if (bf16)
-      hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, true, false>), g3, b3, 0, stream, prm);
-    else
-      hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, false, false>), g3, b3, 0, stream, prm);
+  if constexpr (KP == BV) {
+    if (prm.mmap) {  // segment maps
+      if (bf16)
+        hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, true, false>), g3, b3, 0, stream, prm);
+      else
+        hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, false, false>), g3, b3, 0, stream, prm);
+      return hipGetLastError();
+    }
   }
+  if (bf16)
+    hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, true, true>), g3, b3, 0, stream, prm);
+  else
+    hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, false, true>), g3, b3, 0, stream, prm);
   return hipGetLastError();
 }
 
 // Picks the kernel variant for these sizes and launches it.
 hipError_t launch_variant(Params prm, bool bf16, hipStream_t stream) {
-  const uintptr_t al = (uintptr_t)prm.q | (uintptr_t)prm.k | (uintptr_t)(prm.v_zero ? prm.k : prm.v) | (uintptr_t)prm.g;
+  const uintptr_t al = (uintptr_t)prm.q | (uintptr_t)prm.k | (uintptr_t)prm.v | (uintptr_t)prm.g;
   prm.pair = (prm.K % 2 == 0) && (prm.V % 2 == 0) && (al % 8 == 0);
   prm.ovec = (prm.V % 8 == 0) && ((uintptr_t)prm.out % 16 == 0);
-  const uintptr_t sal = (prm.init_identity ? 0 : (uintptr_t)prm.init) | (uintptr_t)prm.fin | (uintptr_t)prm.ckpt;
+  const uintptr_t sal = (uintptr_t)prm.init | (uintptr_t)prm.fin | (uintptr_t)prm.ckpt | (uintptr_t)prm.mmap;
   prm.svec = (prm.K % 4 == 0) && (sal % 16 == 0);
   if (prm.K <= 64) {
     prm.nvb = (int)((prm.V + 63) / 64);
     return launch_cfg<64, 64>(prm, bf16, stream);
+  }
+  if (prm.mmap) {  // segment maps: the K columns of M need 128-column value blocks
+    prm.nvb = (int)((prm.V + 127) / 128);
+    return launch_cfg<128, 128>(prm, bf16, stream);
   }
   // 128-column value blocks whenever V allows, also for few (sequence, head)
   // chains: 64-column blocks double the workgroups, but each repeats the
@@ -1542,8 +1578,7 @@ hipError_t launch_chunk_prefill(const kda_prefill_args_t& a, hipStream_t stream)
   prm.fin_bf16 = a.final_dtype == KDA_BF16;
   prm.l2norm = a.use_qk_l2norm != 0;
   prm.order = nullptr;
-  prm.v_zero = 0;
-  prm.init_identity = 0;
+  prm.mmap = nullptr;
   prm.nvb = 1;
   prm.ckpt = a.ckpt_states;
   prm.ckpt_cu = a.ckpt_cu;
@@ -1572,24 +1607,18 @@ hipError_t launch_chunk_prefill(const kda_prefill_args_t& a, hipStream_t stream)
     Params seg = prm;
     seg.cu = scu;
     seg.N = L.nmax;
-    // pass 1a: b of every segment
+    // pass 1: the map (M, b) of every segment but the last of its sequence
     Params p1 = seg;
     p1.init = nullptr;
     p1.out = nullptr;
     p1.ckpt = nullptr;
     p1.fin = bmap;
     p1.fin_bf16 = 0;
+    p1.mmap = mmap;
     p1.seq_of = sseq;
     p1.seq_cu = a.cu_seqlens;
     p1.skip_last = 1;
     if ((e = launch_variant(p1, bf16, stream)) != hipSuccess) return e;
-    // pass 1b: M of every segment (identity state, zero values, V = K)
-    Params p2 = p1;
-    p2.V = a.K;
-    p2.v_zero = 1;
-    p2.init_identity = 1;
-    p2.fin = mmap;
-    if ((e = launch_variant(p2, bf16, stream)) != hipSuccess) return e;
     // scan: S_in of every segment, final states
     const int64_t ncb = (a.V + kScanCols - 1) / kScanCols;
     hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)(a.N * a.H * ncb)), dim3(256), 0, stream, sfirst, bmap, mmap,
