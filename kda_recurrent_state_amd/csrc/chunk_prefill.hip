@@ -838,10 +838,12 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
       off = pre[w];  // uniform index: one indexed register move
       gm[cc] = ref * kLog2e;
       gL[cc] = tot * kLog2e;
+      // gx becomes gamma_i - gamma_m = log2(e) * (in-wave prefix + off - ref)
+      const float nref = (off - ref) * kLog2e;
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
-        gx[r][cc] = (gx[r][cc] + off) * kLog2e;
-        guard = fmaxf(guard, fabsf(gx[r][cc] - gm[cc]));
+        gx[r][cc] = fmaf(gx[r][cc], kLog2e, nref);
+        guard = fmaxf(guard, fabsf(gx[r][cc]));
       }
       guard = fmaxf(guard, fmaxf(gm[cc], gL[cc] - gm[cc]));
     }
@@ -866,7 +868,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
         __bf16 kl[CPL], ql[CPL], kr[CPL], qg[CPL];
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) {
-          const float d = gx[r][cc] - gm[cc];
+          const float d = gx[r][cc];                     // gamma_i - gamma_m
           const float e1 = __builtin_amdgcn_exp2f(d);   // 2^(gamma_i - gamma_m)
           const float e2 = __builtin_amdgcn_exp2f(-d);  // 2^(gamma_m - gamma_i)
           const float fkl = kx[r][cc] * e1 * bk;        // beta k^ 2^(gamma_i - gamma_m)
