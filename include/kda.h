@@ -162,6 +162,13 @@ kda_status_t kda_state_scatter(const kda_state_cache_t* cache, const void* indic
  *   out_t = scale * S^T q_t
  * evaluated chunkwise in chunks of 64 tokens aligned to each sequence start
  * ([P3]).  Sequences of length 0 pass their initial state through.
+ * Precision: the state, the gate sums, the row norms, the triangular
+ * inverse's diagonal blocks and every accumulation are fp32; the operands of
+ * the matrix products (the gated q/k tiles, the inverse, W, U, V_new and the
+ * state as a right-hand operand) are rounded to bf16 -- for fp32 q/k/v too.
+ * Against an fp64 evaluation of the recurrence this gives a relative L2
+ * error of about 4e-3 on outputs and final states for bf16 and fp32 inputs
+ * alike (tolerance 2e-2).
  */
 typedef struct {
   int64_t T, N, H, K, V;
