@@ -1369,7 +1369,7 @@ __global__ __launch_bounds__(1024) void seg_plan_kernel(const int32_t* __restric
 // r reads column r: consecutive addresses across lanes) and the next
 // segment's T and b are loaded into registers while this segment's product
 // runs (K % 4 == 0: 16-byte loads; other K: element loads, not prefetched).
-constexpr int kScanCols = 16;
+constexpr int kScanCols = 8;
 constexpr int kScanT = 256;                      // threads
 constexpr int kScanSL = kScanCols + 4;           // sS row stride (16-byte aligned rows)
 constexpr int kScanML = 128 + 4;                 // sT row stride
@@ -1400,7 +1400,7 @@ __global__ __launch_bounds__(kScanT) void seg_scan_kernel(const int32_t* __restr
     sS[c * kScanSL + vl] = x;
   }
   const int r = tid >> 1;                      // this thread's state row (key channel)
-  const int j0 = (tid & 1) * (kScanCols / 2);  // and its 8 columns
+  const int j0 = (tid & 1) * (kScanCols / 2);  // and its kScanCols / 2 columns
   const int64_t s0 = sfirst[n], s1 = sfirst[n + 1];
   f32x4 tr[kScanV4];        // the next segment's T (vector path)
   float br[kScanCols / 2];  // and this thread's b entries
@@ -1453,12 +1453,11 @@ __global__ __launch_bounds__(kScanT) void seg_scan_kernel(const int32_t* __restr
     if (r < K) {
       for (int x = 0; x < K; ++x) {
         const float m = sT[x * kScanML + r];
-        const f32x4 a = *reinterpret_cast<const f32x4*>(sS + x * kScanSL + j0);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(sS + x * kScanSL + j0 + 4);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc[j] += m * a[j];
-          acc[4 + j] += m * b[j];
+        for (int q = 0; q < kScanCols / 8; ++q) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(sS + x * kScanSL + j0 + 4 * q);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[4 * q + j] += m * a[j];
         }
       }
     }
