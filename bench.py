@@ -230,13 +230,28 @@ def calibrate_copy(device, gib: float = 1.0):
     print(json.dumps({"calibration_copy_bytes_read": n * 2, "calibration_copy_bytes_written": n * 2}))
 
 
+WARMUP_MIN_S = 0.25  # every warm-up also runs until this much wall time has passed (clocks settle)
+
+
+def warm_up(fn, warmup: int, min_s: float = WARMUP_MIN_S) -> int:
+    """Run fn() at least ``warmup`` times and for at least ``min_s`` seconds
+    (synchronising every few calls); returns the number of calls made."""
+    import torch
+    n, t0 = 0, time.perf_counter()
+    while n < warmup or time.perf_counter() - t0 < min_s:
+        fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
 def _timed(fn, steps, warmup):
     """Run fn() warmup + steps times; HIP events on the current stream around each call."""
     import torch
     stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
+    warm_up(fn, warmup)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
     for a, b in evs:
@@ -339,9 +354,7 @@ def measure_chunk(dev, seed: int, steps: int, warmup: int, which: str):
         if which == "long":
             kda.kda_state_scatter(cache, si, fin)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, warmup)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
@@ -477,9 +490,7 @@ def bench_ckpt(args, dev, interval: int = 1024):
         if ev is not None:
             ev[3].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, args.warmup)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -574,9 +585,7 @@ def main():
         if ev is not None:
             ev[3].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, args.warmup)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
