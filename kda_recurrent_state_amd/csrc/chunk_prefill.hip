@@ -116,7 +116,8 @@ struct Cfg {
   static constexpr int R_TOT = R_AQK + SZ_A;        // per-wave gate sums fp32 [NW][KP]
   static constexpr int R_DEC = R_TOT + NW * KP * 4; // 2^gamma_L fp32 [KP]
   static constexpr int R_RED = R_DEC + KP * 4;      // range guard fp32 [NW]
-  static constexpr int LDS = R_RED + 64;
+  static constexpr int R_DIAG = R_RED + 64;         // fp32 [64] diagonal of A_qk
+  static constexpr int LDS = R_DIAG + kC * 4;
   static_assert(LDS <= 160 * 1024, "LDS budget");
   static_assert(kC * LDO * 2 <= SZ_ROW, "output staging fits in the KR region");
   static_assert(RPW == 8 || RPW == 16, "rows per wave");
@@ -157,17 +158,17 @@ __device__ __forceinline__ float dpp_rows(float x) {
                             __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, kRowMask, 0xF, false));
 }
 
-// out[r] = 1 / sqrt(sum over the wave's 64 lanes of x[r]) for R rows at once,
-// the same bits in every lane.  Reduce-scatter: the half-wave swap pairs row j
-// with row j + R/2 (lanes 0-31 keep row j, lanes 32-63 row j + R/2), the
-// quarter-wave swap pairs those sums again, so each 16-lane group holds one
-// row of every register; DPP finishes the sums inside the groups, one rsqrt
-// per register covers four rows, and readlane hands each row to the wave.
+// Sums over the wave's 64 lanes of x[r] for R rows at once, reduce-scattered:
+// the half-wave swap pairs row j with row j + R/2 (lanes 0-31 keep row j,
+// lanes 32-63 row j + R/2), the quarter-wave swap pairs those sums again, so
+// each 16-lane group holds one row of every register, and DPP finishes the
+// sums inside the groups.  On return lane group g holds in u[j] the sum of
+// row j + g * R/4, the same bits in each of its 16 lanes.
 template <int R>
-__device__ __forceinline__ void rows_rsqrt(const float (&x)[R], float (&out)[R]) {
+__device__ __forceinline__ void rows_reduce(const float (&x)[R], float (&u)[R / 4]) {
   static_assert(R % 4 == 0, "rows");
   constexpr int R2 = R / 2, R4 = R / 4;
-  float t[R2], u[R4];
+  float t[R2];
 #pragma unroll
   for (int j = 0; j < R2; ++j) {
     const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x[j]),
@@ -188,11 +189,59 @@ __device__ __forceinline__ void rows_rsqrt(const float (&x)[R], float (&out)[R])
     u[j] += dpp<0x4E>(u[j]);   // quad_perm [2,3,0,1]
     u[j] += dpp<0x141>(u[j]);  // row_half_mirror
     u[j] += dpp<0x140>(u[j]);  // row_mirror: every lane of a group holds the group's row
-    u[j] = __frsqrt_rn(u[j]);
   }
-  // group g of u[j] holds row j + g * R4
+}
+
+// out[r] = 1 / sqrt(sum over the wave's 64 lanes of x[r]) for R rows at once,
+// the same bits in every lane: one rsqrt per register of the reduce-scattered
+// sums covers four rows, and readlane hands each row to the wave.
+template <int R>
+__device__ __forceinline__ void rows_rsqrt(const float (&x)[R], float (&out)[R]) {
+  constexpr int R4 = R / 4;
+  float u[R4];
+  rows_reduce(x, u);
+#pragma unroll
+  for (int j = 0; j < R4; ++j) u[j] = __frsqrt_rn(u[j]);
 #pragma unroll
   for (int r = 0; r < R; ++r) out[r] = lane_f(u[r % R4], 16 * (r / R4));
+}
+
+// Per-row factors of a wave's R chunk rows (rows row0 .. row0 + R - 1), from
+// each lane's shares of the row sums sk = |k|^2 (+ eps), sq = |q|^2 (+ eps)
+// and dq = k . q: rk[r] = 1 / |k_r| and rq[r] = 1 / |q_r| (1 without l2norm),
+// the same bits in every lane, and diag[r] = scale q^_r . k^_r, the
+// diagonal of A_qk, written by one lane per row.  That fp32 diagonal replaces
+// the one the operand tiles give: their bf16 rounding errors do not cancel
+// when q^_r . k^_r is small, and that term is the whole output of a
+// sequence's first token when it starts from a zero state.
+template <int R>
+__device__ __forceinline__ void rows_norms_diag(const float (&sk)[R], const float (&sq)[R], const float (&dq)[R],
+                                                bool l2norm, float scale, int lane, float (&rk)[R], float (&rq)[R],
+                                                float* diag) {
+  constexpr int R4 = R / 4;
+  float uk[R4], uq[R4], ud[R4];
+  rows_reduce(dq, ud);
+#pragma unroll
+  for (int j = 0; j < R4; ++j) uk[j] = uq[j] = 1.f;
+  if (l2norm) {
+    rows_reduce(sk, uk);
+    rows_reduce(sq, uq);
+#pragma unroll
+    for (int j = 0; j < R4; ++j) {
+      uk[j] = __frsqrt_rn(uk[j]);
+      uq[j] = __frsqrt_rn(uq[j]);
+      ud[j] *= uk[j] * uq[j];
+    }
+  }
+  if ((lane & 15) == 0) {  // group g holds rows j + g R/4
+#pragma unroll
+    for (int j = 0; j < R4; ++j) diag[j + (lane >> 4) * R4] = ud[j] * scale;
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {  // (1 in every lane without l2norm)
+    rk[r] = lane_f(uk[r % R4], 16 * (r / R4));
+    rq[r] = lane_f(uq[r % R4], 16 * (r / R4));
+  }
 }
 
 // (for x >= 0: rows outside the broadcast masks receive 0)
@@ -411,6 +460,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
   float* sTot = reinterpret_cast<float*>(smem + C::R_TOT);
   float* sDec = reinterpret_cast<float*>(smem + C::R_DEC);
   float* sRed = reinterpret_cast<float*>(smem + C::R_RED);
+  float* sDiag = reinterpret_cast<float*>(smem + C::R_DIAG);
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, provably uniform
@@ -525,13 +575,14 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
   // and r1 are constants at every call, so the loop unrolls to the rows
   // asked for): rows past the span re-read its last row, channels past K and
   // columns past V re-read the last valid one.
-  auto issue_rows = [&](int64_t tb, int r0, int r1) __attribute__((always_inline)) {
+  // (wv: the wave index as the caller has it, opaque inside the chunk loop)
+  auto issue_rows = [&](int64_t tb, int r0, int r1, int wv) __attribute__((always_inline)) {
     const int64_t span = (len - tb) < (int64_t)kC ? (len - tb) : (int64_t)kC;
     if (p.pair) {
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
         if (r < r0 || r >= r1) continue;
-        const int i = RPW * w + r;
+        const int i = RPW * wv + r;
         const int64_t ir = i < span ? i : span - 1;
         // Uniform 64-bit bases at the chunk's first (token, head) row and
         // 32-bit offsets from them (H * max(K, V) <= 2^22 keeps a chunk's
@@ -592,7 +643,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
         if (r < r0 || r >= r1) continue;
-        const int i = RPW * w + r;
+        const int i = RPW * wv + r;
         const int64_t ir = i < span ? i : span - 1;
         const int64_t th = (bos + tb + ir) * H + h;
         raw.b[r] = p.beta_bf16 ? (unsigned)static_cast<const unsigned short*>(p.beta)[th]
@@ -632,7 +683,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
       }
     }
   };
-  auto issue_loads = [&](int64_t tb) __attribute__((always_inline)) { issue_rows(tb, 0, RPW); };
+  auto issue_loads = [&](int64_t tb, int wv) __attribute__((always_inline)) { issue_rows(tb, 0, RPW, wv); };
 
   // Checkpoints: ck_next is the next checkpoint position relative to bos and
   // ck_row its row (both uniform).  Chunks never straddle a multiple of 64
@@ -656,7 +707,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
 
   int64_t t0 = 0;
   int Lcap = kC;
-  if (len > 0) issue_loads(0);
+  if (len > 0) issue_loads(0, w);
   while (t0 < len) {
     // chunk length: the cap, the tokens left, and the next multiple of 64
     int L = (int)((len - t0) < (int64_t)Lcap ? (len - t0) : (int64_t)Lcap);
@@ -670,6 +721,13 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     // loop into a register of its own (which would force spills).
     int tid_i = tid;
     asm volatile("" : "+v"(tid_i));
+    // The wave index, opaque per iteration too: the wave-uniform tile offsets
+    // derived from it are recomputed in each chunk rather than hoisted out of
+    // the loop, where they would stay live in (and spill out of) the scalar
+    // registers.
+    int w_i = w;
+    asm volatile("" : "+s"(w_i));
+    const int w = w_i;
     const int l = tid_i & 63;
     const int lr = l & 15;
     const int lg = l >> 4;
@@ -749,9 +807,9 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
           vx[r][vv] = __uint_as_float(raw.v[r][vv]);
       }
     }
-    // squared row norms of k and q (bf16 pairs: one dot2 per pair), each lane
-    // adding its share of eps
-    float sk[RPW], sq[RPW];
+    // squared row norms of k and q and the dot products k . q (bf16 pairs: one
+    // dot2 per pair), each lane adding its share of eps to the norms
+    float sk[RPW], sq[RPW], dq[RPW];
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       if (kBF16 && CPL == 2) {
@@ -760,13 +818,17 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
                                                 __builtin_bit_cast(bf16x2, raw.k[r][0]), kL2EpsLane, false);
         sq[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, raw.q[r][0]),
                                                 __builtin_bit_cast(bf16x2, raw.q[r][0]), kL2EpsLane, false);
+        dq[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, raw.k[r][0]),
+                                                __builtin_bit_cast(bf16x2, raw.q[r][0]), 0.f, false);
       } else {
         sk[r] = kL2EpsLane;
         sq[r] = kL2EpsLane;
+        dq[r] = 0.f;
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) {
           sk[r] += kx[r][cc] * kx[r][cc];
           sq[r] += qx[r][cc] * qx[r][cc];
+          dq[r] += kx[r][cc] * qx[r][cc];
         }
       }
     }
@@ -798,9 +860,11 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
       *reinterpret_cast<float2*>(sTot + w * KP + c_lo) = float2{tw[0], tw[CPL - 1]};
     else
       sTot[w * KP + c_lo] = tw[0];
-    // 1 / |row| for q and k (1 without l2norm; uniform branch)
+    // 1 / |row| for q and k (1 without l2norm) and the diagonal of A_qk
     float rk[RPW], rq[RPW];
-    if (p.l2norm) {
+    if constexpr (kOut) {
+      rows_norms_diag(sk, sq, dq, p.l2norm != 0, scale, l, rk, rq, sDiag + RPW * w);
+    } else if (p.l2norm) {  // maps: no A_qk
       rows_rsqrt(sk, rk);
       rows_rsqrt(sq, rq);
     } else {
@@ -923,7 +987,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     // their SIMD partners finish phase A; the other half issue theirs after
     // phase B, while wave 0 computes phase C.
     const bool early = w < NW / 2;
-    if (early && t0 + L < len) issue_loads(t0 + L);
+    if (early && t0 + L < len) issue_loads(t0 + L, w);
     lds_barrier();
     {
       // range guard of every wave (written before the barrier above): a span
@@ -936,7 +1000,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
         Lcap = L > 16 ? 16 : (L > 4 ? 4 : 1);
         // this chunk's rows again (the early half has overwritten them; reloading
         // in every wave also ends the rows' live range at phase 0)
-        issue_loads(t0);
+        issue_loads(t0, w);
         continue;
       }
     }
@@ -997,11 +1061,13 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
             for (int e = 0; e < 4; ++e) d[e] = 4 * lg + e > lr ? akk[m][e] : 0.f;
             *reinterpret_cast<f32x4*>(sAd + bi[m] * C::AD_B + lr * C::AD_C + 4 * lg) = d;
           }
-          if constexpr (kOut) {  // row 16bi + lr, columns 16bj + 4lg + e
+          if constexpr (kOut) {  // row 16bi + lr, columns 16bj + 4lg + e; the fp32 diagonal from sDiag
             const int i = 16 * bi[m] + lr, j0 = 16 * bj[m] + 4 * lg;
-            *reinterpret_cast<bf16x4*>(sAqk + i * C::LDA + kpos(j0)) =
-                to_bf16x4(i >= j0 ? aqk[m][0] : 0.f, i >= j0 + 1 ? aqk[m][1] : 0.f, i >= j0 + 2 ? aqk[m][2] : 0.f,
-                          i >= j0 + 3 ? aqk[m][3] : 0.f);
+            f32x4 a;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[e] = i > j0 + e ? aqk[m][e] : 0.f;
+            if (bi[m] == bj[m] && (lr >> 2) == lg) a[lr & 3] = sDiag[i];
+            *reinterpret_cast<bf16x4*>(sAqk + i * C::LDA + kpos(j0)) = to_bf16x4(a[0], a[1], a[2], a[3]);
           }
         }
       };
@@ -1016,7 +1082,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     lds_barrier();
 
     // the other half's loads (they land while phases C-E compute)
-    if (!early && t0 + L < len) issue_loads(t0 + L);
+    if (!early && t0 + L < len) issue_loads(t0 + L, w);
 
     // ---------------- phase C: D_b = (I + A_bb)^-1 for the diagonal blocks --
     if (w == 0) {
@@ -1288,6 +1354,707 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Two workgroups per CU.  The kernel above runs one (sequence, head) chain per
+// CU: its phases follow one another (elementwise VALU work, block products
+// bound by LDS latency, MFMA chains, load issue), and with ~150 KiB of LDS
+// nothing overlaps them.  This variant, for K = V = 128 with bf16 q, k, v,
+// runs a chain with 4 waves (16 chunk rows and 32 value columns each) in at
+// most 80 KiB of LDS, so two chains share each CU and the phases of one fill
+// the gaps of the other.  Arithmetic and operand layouts are those of the
+// kernel above; what changes is where the tiles live:
+//  * tiles are unpadded, bank conflicts avoided by swizzling 16-byte runs
+//    (row-major tiles) or 8-byte runs (transposed tiles);
+//  * the gated tiles of phase B (KL, KR, QL) and those of phases D-E
+//    (beta K 2^gamma, Kbar^T, Qg) share one region: the latter are written
+//    from registers once phase B is done;
+//  * -W is written over beta K 2^gamma: wave w solves, and alone reads, the
+//    32-channel pair w, whose 4 KiB it overwrites (token-major, for phase E);
+//  * A_kk / D_b and A_qk keep only their blocks on or below the diagonal;
+//  * the output staging tile reuses the (beta V)^T region, which the next
+//    chunk's phase 0 writes only after its first barrier.
+// The next chunk's loads are issued after phase E (registers are short before
+// then); the other workgroup on the CU computes while they are in flight.
+// ---------------------------------------------------------------------------
+namespace w2 {
+constexpr int NW = 4, NT = 256, RPW = 16, KT = 8, KS = 4;
+// LDS map, bytes
+constexpr int R1 = 0;        // KL, KR, QL [64][128] each  ->  beta K 2^gamma (-> -W) [128][64], Kbar^T, Qg
+constexpr int R2 = 49152;    // (beta V)^T [128][64]  ->  output staging [64][128]
+constexpr int R_AB = 65536;  // 10 bf16 blocks 16x16: -A_kk below the diagonal, D_b on it
+constexpr int R_AQK = 70656; // 6 bf16 blocks [16][32] of A_qk (kpos columns)
+constexpr int AD_B = 260;    // fp32 stride of the diagonal blocks of A_kk (4 banks apart)
+constexpr int R_AD = 76800;  // fp32 4 x [16 columns][16 rows] diagonal blocks of A_kk  /  gate totals [4][128]
+constexpr int R_DEC = R_AD + 4 * AD_B * 4;  // fp32 [128] 2^gamma_L
+constexpr int R_RED = R_DEC + 512;          // fp32 [4] range guard
+constexpr int R_DIAG = R_RED + 16;          // fp32 [64] diagonal of A_qk
+constexpr int LDS = R_DIAG + 256;
+static_assert(LDS <= 81920, "two workgroups per CU");
+static_assert(NW * 128 <= 4 * AD_B, "gate totals fit in the A_kk diagonal region");
+// [64][128] row-major tiles (KL, KR, QL, Qg, output): 16-byte run of column c
+// in row t XORed with t mod 16
+__device__ __forceinline__ int rs_pos(int t, int c) { return t * 128 + ((((c >> 3) ^ (t & 15)) << 3) | (c & 7)); }
+// [128][64] transposed tiles ((beta V)^T, beta K 2^gamma): rows in pairs of
+// 256 bytes (one sweep of the banks) of 32 runs of 4 tokens; run (r, t) at
+// 16 ((r & 1) ^ bit 5 of r) + ((t >> 2) ^ 2 (bits 1-3 of r) ^ bit 4 of r).
+// The 16 rows x 2 token runs of a 32-lane operand read, and the rows 2l + x
+// of a 32-lane store, fall on distinct banks.
+__device__ __forceinline__ int tu_pos(int r, int t) {
+  const int hi = (r & 1) ^ ((r >> 5) & 1);
+  const int lo = ((t >> 2) ^ (((r >> 1) & 7) << 1) ^ ((r >> 4) & 1)) & 15;
+  return (r >> 1) * 128 + ((hi << 4) | lo) * 4 + (t & 3);
+}
+// -W of channel pair w: [64 tokens][32 kpos channels] over pair w's rows of
+// beta K 2^gamma (elements [2048 w, 2048 w + 2048)); 16-byte runs XORed with
+// bits 2-3 of the token
+__device__ __forceinline__ int w_pos(int t, int kp) { return t * 32 + ((((kp >> 3) ^ ((t >> 2) & 3)) << 3) | (kp & 7)); }
+// A_kk / D_b block (bi >= bj), element (i, j): 8-byte runs XORed with bit 3 of i
+__device__ __forceinline__ int ab_pos(int bi, int bj, int i, int j) {
+  return ((bi * (bi + 1)) / 2 + bj) * 256 + i * 16 + ((((j >> 2) ^ ((i >> 3) << 1)) << 2) | (j & 3));
+}
+// A_qk block of row tile rt and 32-column block q2 (32 q2 <= 16 rt + 15), row
+// i, kpos column kp
+__device__ __forceinline__ int aqk_pos(int q2, int rt, int i, int kp) {
+  return (q2 ? rt + 2 : rt) * 512 + i * 32 + ((((kp >> 3) ^ ((i >> 2) & 3)) << 3) | (kp & 7));
+}
+}  // namespace w2
+
+// Requires K == V == 128, bf16 q/k/v, p.pair, p.ovec, outputs (no maps);
+// kBetaBF16 == p.beta_bf16.
+template <bool kBetaBF16>
+__global__ __launch_bounds__(256, 2) void chunk_prefill_2wg_kernel(Params p) {
+  using namespace w2;
+  __shared__ __attribute__((aligned(16))) char smem[LDS];
+  __bf16* sKL = reinterpret_cast<__bf16*>(smem + R1);
+  __bf16* sKR = reinterpret_cast<__bf16*>(smem + R1 + 16384);
+  __bf16* sQL = reinterpret_cast<__bf16*>(smem + R1 + 32768);
+  __bf16* sKE = reinterpret_cast<__bf16*>(smem + R1);  // -> -W, pair by pair
+  __bf16* sKB = reinterpret_cast<__bf16*>(smem + R1 + 16384);
+  __bf16* sQg = reinterpret_cast<__bf16*>(smem + R1 + 32768);
+  __bf16* sVT = reinterpret_cast<__bf16*>(smem + R2);
+  __bf16* sO = reinterpret_cast<__bf16*>(smem + R2);
+  __bf16* sAb = reinterpret_cast<__bf16*>(smem + R_AB);
+  __bf16* sAqk = reinterpret_cast<__bf16*>(smem + R_AQK);
+  float* sAd = reinterpret_cast<float*>(smem + R_AD);
+  float* sTot = reinterpret_cast<float*>(smem + R_AD);
+  float* sDec = reinterpret_cast<float*>(smem + R_DEC);
+  float* sRed = reinterpret_cast<float*>(smem + R_RED);
+  float* sDiag = reinterpret_cast<float*>(smem + R_DIAG);
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63;
+  const int lr = l & 15;
+  const int lg = l >> 4;
+
+  // ---- work item: one workgroup per (sequence, head) ----
+  const int64_t H = p.H, K = p.K, V = p.V;
+  const int64_t item = blockIdx.x;
+  if (item >= p.N * H) return;
+  const int64_t rank = item / H;
+  const int64_t h = item - rank * H;
+  const int64_t n = p.order ? (int64_t)p.order[rank] : rank;
+  int64_t bos = p.cu[n], eos = p.cu[n + 1];
+  bos = bos < 0 ? 0 : (bos > p.T ? p.T : bos);
+  eos = eos < bos ? bos : (eos > p.T ? p.T : eos);
+  const int64_t len = eos - bos;
+  const int64_t srow = (n * H + h) * V;
+  int64_t frow = srow;
+  bool fin_ok = true;
+  if (p.seq_of) {  // output pass over segments
+    const int64_t sq = p.seq_of[n];
+    int64_t se = p.seq_cu[sq + 1];
+    se = se < 0 ? 0 : (se > p.T ? p.T : se);
+    fin_ok = eos == se && n < (int64_t)*p.seg_total;
+    frow = (sq * H + h) * V;
+  }
+
+  // A_qk: the upper halves of the two diagonal 32-column blocks are read by
+  // the output product but never written
+  for (int e = tid; e < 2 * 16 * 16; e += NT) {
+    const int q2 = e >> 8, i = (e >> 4) & 15, jj = e & 15;
+    sAqk[aqk_pos(q2, 2 * q2, i, kpos(16 + jj))] = (__bf16)0.f;
+  }
+
+  // ---- initial state: S[m][ct][e] = S(c = 16ct + 4lg + e, value column 32w + 16m + lr) ----
+  f32x4 S[2][KT];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int64_t vcol = 32 * w + 16 * m + lr;
+    if (p.init) {
+#pragma unroll
+      for (int ct = 0; ct < KT; ++ct) {
+        const int64_t o = (srow + vcol) * K + 16 * ct + 4 * lg;
+        if (p.svec) {
+          if (p.init_bf16) {
+            const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const unsigned short*>(p.init) + o);
+            S[m][ct] = f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                             __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+          } else {
+            S[m][ct] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.init) + o);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            S[m][ct][e] = p.init_bf16 ? bf2f(static_cast<const unsigned short*>(p.init)[o + e])
+                                      : static_cast<const float*>(p.init)[o + e];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int ct = 0; ct < KT; ++ct) S[m][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
+  const float scale = p.scale;
+  // raw bits of this wave's 16 rows of a chunk: two channels (k, q, g) or
+  // value columns (v) per lane, bf16 pairs in one word
+  unsigned rk_[RPW], rq_[RPW], rv_[RPW], rb_[RPW];
+  float rg_[RPW][2];
+  // This chain's tensors at the current chunk's first (token, head) row; the
+  // pointers advance chunk by chunk, so the loop carries six 64-bit bases
+  // and 32-bit counters only (scalar registers are the scarce resource here).
+  const int64_t crow = bos * H + h;
+  const char* kp = static_cast<const char*>(p.k) + crow * 256;
+  const char* qp = static_cast<const char*>(p.q) + crow * 256;
+  const char* vp = static_cast<const char*>(p.v) + crow * 256;
+  const char* gp = reinterpret_cast<const char*>(p.g) + crow * 512;
+  const char* bp = static_cast<const char*>(p.beta) + crow * (kBetaBF16 ? 2 : 4);
+  char* op = static_cast<char*>(p.out) + crow * 256;
+  const uint32_t Hu = (uint32_t)H;
+  const uint32_t lenu = (uint32_t)len;
+  // Loads of the chunk that starts dr tokens after the current one, span
+  // (1..64) tokens of it: rows past the span re-read its last row.  32-bit
+  // offsets: (dr + 63) H 512 < 2^32 for H <= 65535.
+  // (wv: the wave index as the caller has it, opaque inside the chunk loop)
+  auto issue_loads = [&](uint32_t dr, uint32_t span, int wv) __attribute__((always_inline)) {
+    const uint32_t cl = (uint32_t)(tid & 63) * 2;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const uint32_t i = (uint32_t)(RPW * wv + r);
+      const uint32_t ri = ((i < span ? i : span - 1) + dr) * Hu;  // (token, head) rows after the current one
+      if (kBetaBF16)
+        rb_[r] = ld_at<unsigned short>(bp, 2 * ri);
+      else
+        rb_[r] = ld_at<unsigned>(bp, 4 * ri);
+      const uint32_t ek = ri * 128u + cl;
+      rk_[r] = ld_at<unsigned>(kp, 2 * ek);
+      rq_[r] = ld_at<unsigned>(qp, 2 * ek);
+      rv_[r] = ld_at<unsigned>(vp, 2 * ek);
+      const float2 fg = ld_at<float2>(gp, 4 * ek);
+      rg_[r][0] = fg.x;
+      rg_[r][1] = fg.y;
+    }
+  };
+
+  // checkpoints (32-bit: positions within a sequence, rows of ckpt)
+  uint32_t ck_next = 0xffffffffu, ck_iv = 0;
+  int32_t ck_row = 0, ck_end = 0;
+  if (p.ckpt) {
+    int64_t seq = n, off = 0;
+    if (p.seq_of) {
+      seq = p.seq_of[n];
+      int64_t sb = p.seq_cu[seq];
+      sb = sb < 0 ? 0 : (sb > p.T ? p.T : sb);
+      off = bos - sb;
+    }
+    const int64_t j = off / p.ckpt_iv;
+    ck_next = (uint32_t)((j + 1) * p.ckpt_iv - off);
+    ck_iv = (uint32_t)p.ckpt_iv;
+    ck_row = (int32_t)(p.ckpt_cu[seq] + j);
+    const int64_t ce = p.ckpt_cu[seq + 1];
+    ck_end = (int32_t)(ce < p.num_ckpt ? ce : p.num_ckpt);
+  }
+
+  uint32_t t0 = 0;
+  uint32_t Lcap = kC;
+  if (lenu > 0) issue_loads(0, lenu < (uint32_t)kC ? lenu : (uint32_t)kC, w);
+  while (t0 < lenu) {
+    uint32_t L = lenu - t0 < Lcap ? lenu - t0 : Lcap;
+    L = L < kC - (t0 & (kC - 1)) ? L : kC - (t0 & (kC - 1));
+    int tid_i = tid;
+    asm volatile("" : "+v"(tid_i));
+    // The wave index, opaque per iteration too: the wave-uniform tile offsets
+    // derived from it are recomputed in each chunk rather than hoisted out of
+    // the loop, where they would stay live in (and spill out of) the scalar
+    // registers.
+    int w_i = w;
+    asm volatile("" : "+s"(w_i));
+    const int w = w_i;
+    const int l = tid_i & 63;
+    const int lr = l & 15;
+    const int lg = l >> 4;
+    const int c_lo = 2 * l;  // this lane's channels / value columns in the elementwise phases
+
+    // ---------------- phase 0: unpack, gate sums, norms ----------------
+    if (L != kC) {
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        const bool okr = RPW * w + r < L;  // uniform
+        rb_[r] = okr ? rb_[r] : 0u;
+        rk_[r] = okr ? rk_[r] : 0u;
+        rq_[r] = okr ? rq_[r] : 0u;
+        rv_[r] = okr ? rv_[r] : 0u;
+        rg_[r][0] = okr ? rg_[r][0] : 0.f;
+        rg_[r][1] = okr ? rg_[r][1] : 0.f;
+      }
+    }
+    float gx[RPW][2], bt[RPW];
+    unsigned bvp[RPW];  // beta v of this lane's two value columns, a bf16 pair
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      bt[r] = __uint_as_float(kBetaBF16 ? rb_[r] << 16 : rb_[r]);
+      gx[r][0] = rg_[r][0];
+      gx[r][1] = rg_[r][1];
+      bvp[r] = __builtin_bit_cast(unsigned, bf16x2{(__bf16)(bt[r] * __uint_as_float(rv_[r] << 16)),
+                                                   (__bf16)(bt[r] * __uint_as_float(rv_[r] & 0xffff0000u))});
+    }
+    float sk[RPW], sq[RPW], dq[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      sk[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, rk_[r]), __builtin_bit_cast(bf16x2, rk_[r]),
+                                              kL2EpsLane, false);
+      sq[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, rq_[r]), __builtin_bit_cast(bf16x2, rq_[r]),
+                                              kL2EpsLane, false);
+      dq[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, rk_[r]), __builtin_bit_cast(bf16x2, rq_[r]),
+                                              0.f, false);
+    }
+    float tw[2];
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      float run = 0.f;
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        run += gx[r][cc];
+        gx[r][cc] = run;
+      }
+      tw[cc] = run;
+    }
+    *reinterpret_cast<float2*>(sTot + w * 128 + c_lo) = float2{tw[0], tw[1]};
+    float rkn[RPW], rqn[RPW];
+    rows_norms_diag(sk, sq, dq, p.l2norm != 0, scale, l, rkn, rqn, sDiag + RPW * w);
+    lds_barrier();
+    // (beta V)^T, after the barrier: the region held the previous chunk's
+    // output staging, read before it
+#pragma unroll
+    for (int vv = 0; vv < 2; ++vv) {
+#pragma unroll
+      for (int j = 0; j < RPW / 4; ++j) {
+        bf16x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const unsigned u = bvp[4 * j + e];
+          x[e] = __builtin_bit_cast(__bf16, (unsigned short)(vv ? u >> 16 : u & 0xffffu));
+        }
+        *reinterpret_cast<bf16x4*>(sVT + tu_pos(c_lo + vv, RPW * w + 4 * j)) = x;
+      }
+    }
+
+    // gamma in log2 units relative to the reference row m, the range guard
+    const int mw = L > 32 ? 2 : 1;  // waves whose rows precede the reference row
+    float gm[2], gL[2];
+    float guard = 0.f;
+    float totw[NW][2];
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const float2 t2 = *reinterpret_cast<const float2*>(sTot + ww * 128 + c_lo);
+      totw[ww][0] = t2.x;
+      totw[ww][1] = t2.y;
+    }
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      float pre[NW + 1];
+      pre[0] = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) pre[ww + 1] = pre[ww] + totw[ww][cc];
+      const float tot = pre[NW];
+      const float ref = mw == 2 ? pre[2] : pre[1];
+      float off = pre[0];
+      off = pre[w];
+      gm[cc] = ref * kLog2e;
+      gL[cc] = tot * kLog2e;
+      const float nref = (off - ref) * kLog2e;
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        gx[r][cc] = fmaf(gx[r][cc], kLog2e, nref);
+        guard = fmaxf(guard, fabsf(gx[r][cc]));
+      }
+      guard = fmaxf(guard, fmaxf(gm[cc], gL[cc] - gm[cc]));
+    }
+    guard = wave_max(guard);
+    if (l == 0) sRed[w] = guard;
+
+    // ---------------- phase A: KL, KR, QL; KE, KB, Qg kept as bf16 pairs ----
+    unsigned kep[RPW], kbp[RPW], qgp[RPW];
+    {
+      float cg[2], cb[2];
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        cg[cc] = __builtin_amdgcn_exp2f(gm[cc]);           // 2^gamma_m
+        cb[cc] = __builtin_amdgcn_exp2f(gL[cc] - gm[cc]);  // 2^(gamma_L - gamma_m)
+        if (w == 0) sDec[c_lo + cc] = __builtin_amdgcn_exp2f(gL[cc]);
+      }
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        const int i = RPW * w + r;
+        const float bk = bt[r] * rkn[r];
+        const float sqr = scale * rqn[r];
+        float fkl[2], fkr[2], fql[2];
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          const float kx = __uint_as_float(cc == 0 ? rk_[r] << 16 : rk_[r] & 0xffff0000u);
+          const float qx = __uint_as_float(cc == 0 ? rq_[r] << 16 : rq_[r] & 0xffff0000u);
+          const float d = gx[r][cc];                     // gamma_i - gamma_m
+          const float e1 = __builtin_amdgcn_exp2f(d);
+          const float e2 = __builtin_amdgcn_exp2f(-d);
+          fkl[cc] = kx * e1 * bk;      // beta k^ 2^(gamma_i - gamma_m)
+          fkr[cc] = kx * e2 * rkn[r];  // k^ 2^(gamma_m - gamma_i)
+          fql[cc] = qx * e1 * sqr;     // scale q^ 2^(gamma_i - gamma_m)
+        }
+        *reinterpret_cast<bf16x2*>(sKL + rs_pos(i, c_lo)) = bf16x2{(__bf16)fkl[0], (__bf16)fkl[1]};
+        *reinterpret_cast<bf16x2*>(sKR + rs_pos(i, c_lo)) = bf16x2{(__bf16)fkr[0], (__bf16)fkr[1]};
+        *reinterpret_cast<bf16x2*>(sQL + rs_pos(i, c_lo)) = bf16x2{(__bf16)fql[0], (__bf16)fql[1]};
+        kep[r] = __builtin_bit_cast(unsigned, bf16x2{(__bf16)(fkl[0] * cg[0]), (__bf16)(fkl[1] * cg[1])});
+        kbp[r] = __builtin_bit_cast(unsigned, bf16x2{(__bf16)(fkr[0] * cb[0]), (__bf16)(fkr[1] * cb[1])});
+        qgp[r] = __builtin_bit_cast(unsigned, bf16x2{(__bf16)(fql[0] * cg[0]), (__bf16)(fql[1] * cg[1])});
+        // packed here: left to itself the compiler keeps the six fp32
+        // products live through phase B and converts them at their stores
+        asm volatile("" : "+v"(kep[r]), "+v"(kbp[r]), "+v"(qgp[r]));
+      }
+    }
+    lds_barrier();
+    bool retry;
+    {
+      // range guard of every wave: a span whose gate factors would leave
+      // 2^+-100 is re-processed as shorter chunks
+      float gmax = sRed[0];
+#pragma unroll
+      for (int ww = 1; ww < NW; ++ww) gmax = fmaxf(gmax, sRed[ww]);
+      retry = gmax > kRangeLimit && L > 1;
+    }
+    // The next rows are loaded at one place for both paths (below): the
+    // structurised control flow of a `continue`, or of loads on both sides
+    // of an if/else, keeps the words loaded on one path live (undefined)
+    // through the other path's phases.
+    uint32_t dr = 0;  // the chunk whose rows are loaded next starts dr tokens after this one
+    if (retry) {
+      Lcap = L > 16 ? 16 : (L > 4 ? 4 : 1);
+    } else {
+      // ---------------- phase B: A_kk (fp32 diagonal / bf16 below) and A_qk ----
+      {
+        const int wr = (w + 2) & 3;  // the three-pair waves are 2 and 3 (wave 0 goes on to phase C)
+        auto pairs = [&](auto npc) __attribute__((always_inline)) {
+          constexpr int NP = decltype(npc)::value;
+          int bi[NP], bj[NP];
+#pragma unroll
+          for (int m = 0; m < NP; ++m) {
+            const int pr = wr + m * NW;
+            bi[m] = pr >= 6 ? 3 : (pr >= 3 ? 2 : (pr >= 1 ? 1 : 0));
+            bj[m] = pr - (bi[m] * (bi[m] + 1)) / 2;
+          }
+          f32x4 akk[NP], aqk[NP];
+          bf16x8 oL[2][NP], oR[2][NP], oQ[2][NP];
+          auto fetch = [&](int ks, int bf) __attribute__((always_inline)) {
+#pragma unroll
+            for (int m = 0; m < NP; ++m) {
+              oR[bf][m] = ld8(sKR + rs_pos(16 * bj[m] + lr, 32 * ks + 8 * lg));
+              oL[bf][m] = ld8(sKL + rs_pos(16 * bi[m] + lr, 32 * ks + 8 * lg));
+              oQ[bf][m] = ld8(sQL + rs_pos(16 * bi[m] + lr, 32 * ks + 8 * lg));
+            }
+          };
+#pragma unroll
+          for (int m = 0; m < NP; ++m) {
+            akk[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+            aqk[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+          fetch(0, 0);
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 1 < KS) fetch(ks + 1, (ks + 1) & 1);
+#pragma unroll
+            for (int m = 0; m < NP; ++m) {
+              akk[m] = mfma(oL[ks & 1][m], oR[ks & 1][m], akk[m]);
+              aqk[m] = mfma(oR[ks & 1][m], oQ[ks & 1][m], aqk[m]);
+            }
+          }
+#pragma unroll
+          for (int m = 0; m < NP; ++m) {
+            if (bi[m] != bj[m]) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) sAb[ab_pos(bi[m], bj[m], 4 * lg + e, lr)] = (__bf16)(-akk[m][e]);
+            } else {  // rows 4lg..4lg+3 of column lr, fp32, one 16-byte store
+              f32x4 d;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) d[e] = 4 * lg + e > lr ? akk[m][e] : 0.f;
+              *reinterpret_cast<f32x4*>(sAd + bi[m] * AD_B + lr * 16 + 4 * lg) = d;
+            }
+            // A_qk row 16bi + lr, columns 16bj + 4lg + e: kpos 8lg + 4(bj & 1) + e of 32-block bj >> 1;
+            // the fp32 diagonal from sDiag
+            const int i = 16 * bi[m] + lr, j0 = 16 * bj[m] + 4 * lg;
+            f32x4 a;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[e] = i > j0 + e ? aqk[m][e] : 0.f;
+            if (bi[m] == bj[m] && (lr >> 2) == lg) a[lr & 3] = sDiag[i];
+            *reinterpret_cast<bf16x4*>(sAqk + aqk_pos(bj[m] >> 1, bi[m], lr, 8 * lg + 4 * (bj[m] & 1))) =
+                to_bf16x4(a[0], a[1], a[2], a[3]);
+          }
+        };
+        if (wr < 2)
+          pairs(std::integral_constant<int, 3>{});
+        else
+          pairs(std::integral_constant<int, 2>{});
+      }
+      lds_barrier();
+
+      // ---------------- KE, KB, Qg over KL, KR, QL; phase C ------------------
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) *reinterpret_cast<unsigned*>(sQg + rs_pos(RPW * w + r, kpos(c_lo))) = qgp[r];
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+#pragma unroll
+        for (int j = 0; j < RPW / 4; ++j) {
+          bf16x4 xe, xb;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const unsigned ue = kep[4 * j + e], ub = kbp[4 * j + e];
+            xe[e] = __builtin_bit_cast(__bf16, (unsigned short)(cc ? ue >> 16 : ue & 0xffffu));
+            xb[e] = __builtin_bit_cast(__bf16, (unsigned short)(cc ? ub >> 16 : ub & 0xffffu));
+          }
+          *reinterpret_cast<bf16x4*>(sKE + tu_pos(c_lo + cc, RPW * w + 4 * j)) = xe;
+          *reinterpret_cast<bf16x4*>(sKB + kb_pos(c_lo + cc, RPW * w + 4 * j)) = xb;
+        }
+      }
+      if (w == 0) {
+        // D_b = (I + A_bb)^-1 by fp32 forward substitution; lane = (block, column)
+        const int bb = l >> 4;
+        int col = l & 15;
+        asm volatile("" : "+v"(col));
+        const f32x4* Ab = reinterpret_cast<const f32x4*>(sAd + bb * AD_B);
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = (i == col) ? 1.f : 0.f;
+        f32x4 cur[4], nxt[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cur[q] = Ab[q];
+#pragma unroll
+        for (int j = 0; j < 15; ++j) {
+          if (j < 14) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (4 * q + 3 > j + 1) nxt[q] = Ab[(j + 1) * 4 + q];
+          }
+#pragma unroll
+          for (int i = j + 1; i < 16; ++i) x[i] -= cur[i >> 2][i & 3] * x[j];
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) cur[q] = nxt[q];
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sAb[ab_pos(bb, bb, i, col)] = (__bf16)x[i];
+      }
+      lds_barrier();
+
+      // ---------------- phase D: [W | U] = (I + A_kk)^-1 [beta K 2^gamma | beta V] --
+      // wave w: the W tiles of channels 32w + 16m + lr (m = 0, 1) and the U
+      // tiles of its value columns 32w + 16m + lr (m = 2, 3), four independent
+      // chains of the blocked substitution X_b = D_b (R_b - sum_{c<b} A_bc X_c).
+      // Each W block is also taken transposed (operands swapped), so that a lane
+      // holds four consecutive channels of one token, and stored as -W at once
+      // over this wave's own pair of beta K 2^gamma (all of it read up front).
+      f32x4 U[2][4];
+      {
+        s16x4 ab[4][4];
+        bf16x4 rb[4][4];
+#pragma unroll
+        for (int bk = 0; bk < 4; ++bk) {
+#pragma unroll
+          for (int c = 0; c <= bk; ++c) ab[bk][c] = ld4s(sAb + ab_pos(bk, c, lr, 4 * lg));
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            rb[m][bk] = *reinterpret_cast<const bf16x4*>(sKE + tu_pos(32 * w + 16 * m + lr, 16 * bk + 4 * lg));
+            rb[2 + m][bk] = *reinterpret_cast<const bf16x4*>(sVT + tu_pos(32 * w + 16 * m + lr, 16 * bk + 4 * lg));
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        s16x4 xb[4][4];
+#pragma unroll
+        for (int bk = 0; bk < 4; ++bk) {
+          f32x4 acc[4];
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            acc[m] = f32x4{(float)rb[m][bk][0], (float)rb[m][bk][1], (float)rb[m][bk][2], (float)rb[m][bk][3]};
+#pragma unroll
+          for (int c = 0; c < bk; ++c) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) acc[m] = mfma16(ab[bk][c], xb[m][c], acc[m]);
+          }
+          const s16x4 d = ab[bk][bk];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const s16x4 r = pack4(acc[m]);
+            const f32x4 x = mfma16(d, r, f32x4{0.f, 0.f, 0.f, 0.f});
+            if (bk < 3) xb[m][bk] = pack4(x);
+            if (m >= 2) {
+              U[m - 2][bk] = x;
+            } else {
+              const f32x4 xt = mfma16(r, d, f32x4{0.f, 0.f, 0.f, 0.f});
+              *reinterpret_cast<bf16x4*>(sKE + 2048 * w + w_pos(16 * bk + lr, 8 * lg + 4 * m)) =
+                  to_bf16x4(-xt[0], -xt[1], -xt[2], -xt[3]);
+            }
+          }
+        }
+      }
+      lds_barrier();
+
+      // ---------------- phase E: the serial chain on this wave's 32 columns ----
+      // V_new = U - W S, O = Qg S + A_qk V_new, S = D S + Kbar^T V_new; each LDS
+      // operand read serves both column tiles.  The output is computed
+      // transposed, O^T = S^T Qg^T + V_new^T A_qk^T: tile rt holds, per lane,
+      // value columns 32w + 16m + 4lg.. of token 16rt + lr.  The two products
+      // with S run together, one contraction step at a time, the next step's
+      // W and Qg operands read ahead.
+      f32x4 (&Vn)[2][4] = U;
+      f32x4 O[2][4];
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) O[m][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      {
+        bf16x8 aw[2][4], aq[2][4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          aw[0][rt] = ld8(sKE + w_pos(16 * rt + lr, 8 * lg));
+          aq[0][rt] = ld8(sQg + rs_pos(16 * rt + lr, 8 * lg));
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if (ks + 1 < KS) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+              aw[(ks + 1) & 1][rt] = ld8(sKE + 2048 * (ks + 1) + w_pos(16 * rt + lr, 8 * lg));
+              aq[(ks + 1) & 1][rt] = ld8(sQg + rs_pos(16 * rt + lr, 32 * (ks + 1) + 8 * lg));
+            }
+          }
+          const bf16x8 b0 = pack_perm(S[0][2 * ks], S[0][2 * ks + 1]);
+          const bf16x8 b1 = pack_perm(S[1][2 * ks], S[1][2 * ks + 1]);
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) {
+            Vn[0][rt] = mfma(aw[ks & 1][rt], b0, Vn[0][rt]);
+            Vn[1][rt] = mfma(aw[ks & 1][rt], b1, Vn[1][rt]);
+            O[0][rt] = mfma(b0, aq[ks & 1][rt], O[0][rt]);
+            O[1][rt] = mfma(b1, aq[ks & 1][rt], O[1][rt]);
+          }
+        }
+      }
+      bf16x8 bV[2][2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) bV[m][q2] = pack_perm(Vn[m][2 * q2], Vn[m][2 * q2 + 1]);
+      {
+        bf16x8 aq[6];
+#pragma unroll
+        for (int t = 0; t < 6; ++t) {
+          const int q2 = t < 4 ? 0 : 1, rt = t < 4 ? t : t - 2;
+          aq[t] = ld8(sAqk + aqk_pos(q2, rt, lr, 8 * lg));
+        }
+#pragma unroll
+        for (int t = 0; t < 6; ++t) {
+          const int q2 = t < 4 ? 0 : 1, rt = t < 4 ? t : t - 2;
+          O[0][rt] = mfma(bV[0][q2], aq[t], O[0][rt]);
+          O[1][rt] = mfma(bV[1][q2], aq[t], O[1][rt]);
+        }
+      }
+      {
+        // S = D S + Kbar^T V_new: a ring of four Kbar^T operands in flight
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct) {
+          const f32x4 dec = *reinterpret_cast<const f32x4*>(sDec + 16 * ct + 4 * lg);
+          S[0][ct] *= dec;
+          S[1][ct] *= dec;
+        }
+        constexpr int NU = 2 * KT;
+        const int kb0 = lr * kC + 8 * (lg ^ ((lr >> 1) & 7)), kb1 = lr * kC + 8 * ((4 + lg) ^ ((lr >> 1) & 7));
+        bf16x8 kr[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) kr[t] = ld8(sKB + 16 * kC * (t % KT) + (t / KT ? kb1 : kb0));
+#pragma unroll
+        for (int t = 0; t < NU; ++t) {
+          const int q2 = t / KT, ct = t % KT;
+          S[0][ct] = mfma(kr[t & 3], bV[0][q2], S[0][ct]);
+          S[1][ct] = mfma(kr[t & 3], bV[1][q2], S[1][ct]);
+          if (t + 4 < NU) {
+            const int q2n = (t + 4) / KT, ctn = (t + 4) % KT;
+            kr[t & 3] = ld8(sKB + 16 * kC * ctn + (q2n ? kb1 : kb0));
+          }
+        }
+      }
+      // ---------------- output rows of this chunk ---------------------------
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+          *reinterpret_cast<bf16x4*>(sO + rs_pos(16 * rt + lr, 32 * w + 16 * m + 4 * lg)) =
+              to_bf16x4(O[m][rt][0], O[m][rt][1], O[m][rt][2], O[m][rt][3]);
+      dr = L;
+    }
+    // the next chunk's rows (zeros past the end: the loaded words then hold
+    // constants, not this chunk's values, across the loop's back edge)
+    if (t0 + dr < lenu) {
+      const uint32_t left = lenu - t0 - dr;
+      issue_loads(dr, left < (uint32_t)kC ? left : (uint32_t)kC, w);
+    } else {
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        rk_[r] = rq_[r] = rv_[r] = rb_[r] = 0u;
+        rg_[r][0] = rg_[r][1] = 0.f;
+      }
+    }
+    if (!retry) {
+      lds_barrier();
+      {
+        // 32-bit lane offsets from the chain's output pointer
+        const uint32_t row_b = Hu * 256;
+#pragma unroll
+        for (int u0 = 0; u0 < kC * 16; u0 += NT) {
+          const int u = u0 + tid_i;
+          const int i = u >> 4, cv = u & 15;
+          if ((uint32_t)i < L)
+            *reinterpret_cast<bf16x8*>(op + ((uint32_t)i * row_b + 16 * (uint32_t)cv)) = ld8(sO + rs_pos(i, 8 * cv));
+        }
+      }
+      // advance the chain's pointers past this chunk
+      const int64_t adv = (int64_t)L * H;
+      kp += adv * 256;
+      qp += adv * 256;
+      vp += adv * 256;
+      gp += adv * 512;
+      bp += adv * (kBetaBF16 ? 2 : 4);
+      op += adv * 256;
+      t0 += L;
+      Lcap = kC;
+      if (t0 == ck_next) {
+        if (ck_row >= 0 && ck_row < ck_end) {
+          int tid_c = tid;
+          asm volatile("" : "+v"(tid_c));
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+            store_state(S[m], p.ckpt, p.ckpt_bf16, p.svec, ((int64_t)ck_row * H + h) * V, (tid_c & 63) >> 4,
+                        32 * w + 16 * m + (tid_c & 15), K, V);
+        }
+        ck_next += ck_iv;
+        ++ck_row;
+      }
+    }
+  }
+
+  if (p.fin && fin_ok) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) store_state(S[m], p.fin, p.fin_bf16, p.svec, frow, lg, 32 * w + 16 * m + lr, K, V);
+  }
+}
+
 constexpr int64_t kPlanMaxN = 2048;
 constexpr int32_t kMinSplit = 3;  // fewest segments of the longest sequence worth the map passes
 
@@ -1468,6 +2235,15 @@ __global__ __launch_bounds__(kScanT) void seg_scan_kernel(const int32_t* __restr
   }
 }
 
+// Batches of at least this many (sequence, head) chains with K = V = 128 and
+// bf16 q/k/v run two chains per CU (chunk_prefill_2wg_kernel), four chains
+// per CU of the 256.  With fewer, CUs sit at one chain or idle, and one chain
+// on 4 waves is about a third slower than on the 8 waves of
+// chunk_prefill_kernel (H = 32, K = V = 128: 4x8192 and 8x4096 tokens +31-35 %,
+// 16x2048 -6 %, 24x2048 +0 %, 32x2048 -8 %, 64x1024 -11 %, 200 sequences of
+// 64-8192 tokens -12 %).
+constexpr int64_t kTwoPerCuMinChains = 1024;
+
 template <int KP, int BV>
 hipError_t launch_cfg(const Params& prm, bool bf16, hipStream_t stream) {
   const int64_t items = prm.N * prm.H;
@@ -1481,6 +2257,16 @@ hipError_t launch_cfg(const Params& prm, bool bf16, hipStream_t stream) {
         hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, true, false>), g3, b3, 0, stream, prm);
       else
         hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, false, false>), g3, b3, 0, stream, prm);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (KP == 128 && BV == 128) {
+    if (bf16 && prm.K == 128 && prm.V == 128 && prm.pair && prm.ovec && items >= kTwoPerCuMinChains &&
+        prm.T <= INT32_MAX && prm.H <= 65535) {
+      if (prm.beta_bf16)
+        hipLaunchKernelGGL(chunk_prefill_2wg_kernel<true>, dim3((unsigned)items), dim3(w2::NT), 0, stream, prm);
+      else
+        hipLaunchKernelGGL(chunk_prefill_2wg_kernel<false>, dim3((unsigned)items), dim3(w2::NT), 0, stream, prm);
       return hipGetLastError();
     }
   }

@@ -69,6 +69,7 @@ def _check_checkpoints(inp, interval, ckpt_dtype="f32"):
     ([300, 64, 129, 0, 700, 63], 2, 128, 128, "bf16", 64, "f32"),
     ([300, 64, 129, 0, 700], 3, 64, 48, "f32", 128, "bf16"),
     ([520, 1000, 191], 2, 32, 64, "bf16", 192, "f32"),
+    ([0, 1, 64, 65, 300] + [40 + 7 * i for i in range(59)], 16, 128, 128, "bf16", 64, "bf16"),  # two chains per CU
 ])
 def test_checkpoints_match_prefix_states(lengths, H, K, V, dtype, interval, ckpt_dtype):
     inp = wl.host_prefill_inputs(lengths, H, K, V, dtype=dtype, seed=sum(lengths) + interval)

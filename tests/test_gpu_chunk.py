@@ -5,7 +5,9 @@ tiles, ragged tails, K != V, V-split blocks, zero-length sequences, fp32 and
 bf16 I/O, vector and element-by-element loads (odd K or V, sizes that are not
 a multiple of 4, unaligned tensors), no initial state, bf16 final states, out
 aliasing v, final states written in place over the initial states, strong
-decays that force shorter chunks, split/resume and determinism.
+decays that force shorter chunks, split/resume and determinism, on both
+kernels for K = V = 128 (one chain per CU below 1024 (sequence, head) chains,
+two per CU from there on).
 """
 import numpy as np
 import pytest
@@ -143,6 +145,53 @@ def test_many_chains_take_full_value_blocks():
     _check(inp)
 
 
+# Two chains per CU (K = V = 128, bf16 q/k/v, at least 1024 (sequence, head)
+# chains): 64 ragged sequences, among them empty, single-token and exact
+# chunk-multiple ones, x 16 heads.
+TWO_PER_CU = [0, 1, 64, 65, 128] + [40 + 3 * i for i in range(59)]
+
+
+@pytest.mark.parametrize("variant", ["plain", "bf16_final_no_initial", "alias", "no_l2norm"])
+def test_two_chains_per_cu(variant):
+    inp = wl.host_prefill_inputs(TWO_PER_CU, 16, 128, 128, dtype="bf16", seed=61,
+                                 initial=variant != "bf16_final_no_initial")
+    if variant == "no_l2norm":
+        # unnormalised keys need beta * |k|^2 < 2 for a stable state: shrink k
+        # (by a power of two, so the bf16 bits the device gets stay exact)
+        inp["k"] = inp["k"] * np.float32(1.0 / 16.0)
+        inp["k_bits"] = wl.f32_to_bf16_bits(inp["k"])
+        _check(inp, scale=1.0, l2norm=False)
+    elif variant == "bf16_final_no_initial":
+        _check(inp, final_dtype="bf16")
+    else:
+        _check(inp, alias=variant == "alias")
+
+
+@pytest.mark.parametrize("gval", [-30.0, -1e4])
+def test_two_chains_per_cu_strong_decay(gval):
+    inp = wl.host_prefill_inputs(TWO_PER_CU, 16, 128, 128, dtype="bf16", seed=62)
+    g = inp["g"].copy()
+    g[::7, :, ::3] = gval
+    inp["g"] = g
+    _check(inp)
+
+
+def test_two_chains_per_cu_bf16_beta():
+    import torch
+    import kda_recurrent_state_amd as kda
+    from tests.helpers import bf16_tensor
+    inp = wl.host_prefill_inputs(TWO_PER_CU, 16, 128, 128, dtype="bf16", seed=63)
+    bits = wl.f32_to_bf16_bits(inp["beta"].astype(np.float32))
+    inp["beta"] = wl.bf16_bits_to_f32(bits).reshape(inp["beta"].shape)
+    print("case: bf16 beta, two chains per CU", flush=True)
+    d = device_inputs(inp)
+    beta = bf16_tensor(bits).reshape(inp["beta"].shape)
+    o, f = kda.kda_chunk_prefill(d["q"], d["k"], d["v"], d["g"], beta, d["cu_seqlens"], initial_state=d["initial"])
+    torch.cuda.synchronize()
+    ro, rf = _ref(inp)
+    assert_chains(tensor_f64(o), ro, inp["cu_seqlens"], tensor_f64(f), rf)
+
+
 def test_zero_length_sequences_pass_state_through():
     inp = wl.host_prefill_inputs([5, 0, 70, 0], 2, 64, 64, dtype="bf16", seed=7)
     o, f = _run(inp)
@@ -156,10 +205,14 @@ def test_no_initial_state_and_bf16_final():
     _check(inp, final_dtype="bf16")
 
 
-def test_scale_one_and_no_l2norm():
-    inp = wl.host_prefill_inputs([90], 2, 64, 64, dtype="f32", seed=9)
+@pytest.mark.parametrize("lengths,K,V,dtype", [([90], 64, 64, "f32"), ([90, 200], 128, 128, "bf16")])
+def test_scale_one_and_no_l2norm(lengths, K, V, dtype):
+    inp = wl.host_prefill_inputs(lengths, 2, K, V, dtype=dtype, seed=9)
     # unnormalised keys need beta * |k|^2 < 2 for a stable state: shrink k
-    inp["k"] = inp["k"] * np.float32(1.0 / 8.0)
+    # (by a power of two, so bf16 bits stay exact)
+    inp["k"] = inp["k"] * np.float32(1.0 / 16.0)
+    if dtype == "bf16":
+        inp["k_bits"] = wl.f32_to_bf16_bits(inp["k"])
     _check(inp, scale=1.0, l2norm=False)
 
 
@@ -221,8 +274,9 @@ def test_split_and_resume(split):
     assert_chains(tensor_f64(torch.cat([o1, o2])), ro, cu, tensor_f64(f2), rf, label="resumed vs oracle: ")
 
 
-def test_deterministic():
-    inp = wl.host_prefill_inputs([300, 77], 4, 128, 128, dtype="bf16", seed=15)
+@pytest.mark.parametrize("lengths,H", [([300, 77], 4), (TWO_PER_CU, 16)])
+def test_deterministic(lengths, H):
+    inp = wl.host_prefill_inputs(lengths, H, 128, 128, dtype="bf16", seed=15)
     o1, f1 = _run(inp)
     o2, f2 = _run(inp)
     assert np.array_equal(o1, o2) and np.array_equal(f1, f2)
