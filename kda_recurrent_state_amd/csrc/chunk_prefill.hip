@@ -212,8 +212,10 @@ __device__ __forceinline__ void rows_rsqrt(const float (&x)[R], float (&out)[R])
 // the same bits in every lane, and diag[r] = scale q^_r . k^_r, the
 // diagonal of A_qk, written by one lane per row.  That fp32 diagonal replaces
 // the one the operand tiles give: their bf16 rounding errors do not cancel
-// when q^_r . k^_r is small, and that term is the whole output of a
-// sequence's first token when it starts from a zero state.
+// when q^_r . k^_r is small.  It matters only where that term is a token's
+// whole output -- a sequence's first token from a zero state; every later
+// token also sees earlier tokens or the state -- so the kernels compute it in
+// each work item's first chunk only.
 template <int R>
 __device__ __forceinline__ void rows_norms_diag(const float (&sk)[R], const float (&sq)[R], const float (&dq)[R],
                                                 bool l2norm, float scale, int lane, float (&rk)[R], float (&rq)[R],
@@ -860,11 +862,13 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
       *reinterpret_cast<float2*>(sTot + w * KP + c_lo) = float2{tw[0], tw[CPL - 1]};
     else
       sTot[w * KP + c_lo] = tw[0];
-    // 1 / |row| for q and k (1 without l2norm) and the diagonal of A_qk
+    // 1 / |row| for q and k (1 without l2norm) and, in the first chunk, the
+    // diagonal of A_qk (uniform branches)
     float rk[RPW], rq[RPW];
-    if constexpr (kOut) {
+    const bool exact_diag = kOut && t0 == 0;
+    if (exact_diag) {
       rows_norms_diag(sk, sq, dq, p.l2norm != 0, scale, l, rk, rq, sDiag + RPW * w);
-    } else if (p.l2norm) {  // maps: no A_qk
+    } else if (p.l2norm) {
       rows_rsqrt(sk, rk);
       rows_rsqrt(sq, rq);
     } else {
@@ -1065,8 +1069,8 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
             const int i = 16 * bi[m] + lr, j0 = 16 * bj[m] + 4 * lg;
             f32x4 a;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) a[e] = i > j0 + e ? aqk[m][e] : 0.f;
-            if (bi[m] == bj[m] && (lr >> 2) == lg) a[lr & 3] = sDiag[i];
+            for (int e = 0; e < 4; ++e) a[e] = i >= j0 + e ? aqk[m][e] : 0.f;
+            if (exact_diag && bi[m] == bj[m] && (lr >> 2) == lg) a[lr & 3] = sDiag[i];
             *reinterpret_cast<bf16x4*>(sAqk + i * C::LDA + kpos(j0)) = to_bf16x4(a[0], a[1], a[2], a[3]);
           }
         }
@@ -1404,18 +1408,27 @@ __device__ __forceinline__ int tu_pos(int r, int t) {
   const int lo = ((t >> 2) ^ (((r >> 1) & 7) << 1) ^ ((r >> 4) & 1)) & 15;
   return (r >> 1) * 128 + ((hi << 4) | lo) * 4 + (t & 3);
 }
+// Bank rules (gfx950, measured): 32 banks of 4 bytes; a read is served per
+// half-wave, a 16-byte write per 8 lanes and an 8-byte write per 16 lanes.
 // -W of channel pair w: [64 tokens][32 kpos channels] over pair w's rows of
 // beta K 2^gamma (elements [2048 w, 2048 w + 2048)); 16-byte runs XORed with
-// bits 2-3 of the token
-__device__ __forceinline__ int w_pos(int t, int kp) { return t * 32 + ((((kp >> 3) ^ ((t >> 2) & 3)) << 3) | (kp & 7)); }
+// bits 1-2 of the token, which keeps the 16 rows x 2 runs of a half-wave's
+// operand read off each other's banks
+__device__ __forceinline__ int w_pos(int t, int kp) { return t * 32 + ((((kp >> 3) ^ ((t >> 1) & 3)) << 3) | (kp & 7)); }
 // A_kk / D_b block (bi >= bj), element (i, j): 8-byte runs XORed with bit 3 of i
 __device__ __forceinline__ int ab_pos(int bi, int bj, int i, int j) {
   return ((bi * (bi + 1)) / 2 + bj) * 256 + i * 16 + ((((j >> 2) ^ ((i >> 3) << 1)) << 2) | (j & 3));
 }
 // A_qk block of row tile rt and 32-column block q2 (32 q2 <= 16 rt + 15), row
-// i, kpos column kp
+// i, kpos column kp; swizzled as -W
 __device__ __forceinline__ int aqk_pos(int q2, int rt, int i, int kp) {
-  return (q2 ? rt + 2 : rt) * 512 + i * 32 + ((((kp >> 3) ^ ((i >> 2) & 3)) << 3) | (kp & 7));
+  return (q2 ? rt + 2 : rt) * 512 + i * 32 + ((((kp >> 3) ^ ((i >> 1) & 3)) << 3) | (kp & 7));
+}
+// fp32 diagonal block b of A_kk, element (row, col): columns of 16 floats,
+// the 16-byte row groups XORed with bits 1-2 of the column (the 16-byte
+// column stores of phase B then hit distinct banks)
+__device__ __forceinline__ int ad_pos(int b, int row, int col) {
+  return b * AD_B + col * 16 + ((((row >> 2) ^ (col >> 1)) & 3) << 2) + (row & 3);
 }
 }  // namespace w2
 
@@ -1632,8 +1645,18 @@ __global__ __launch_bounds__(256, 2) void chunk_prefill_2wg_kernel(Params p) {
       tw[cc] = run;
     }
     *reinterpret_cast<float2*>(sTot + w * 128 + c_lo) = float2{tw[0], tw[1]};
+    // 1 / |row| for q and k and, in the first chunk, the diagonal of A_qk
     float rkn[RPW], rqn[RPW];
-    rows_norms_diag(sk, sq, dq, p.l2norm != 0, scale, l, rkn, rqn, sDiag + RPW * w);
+    const bool exact_diag = t0 == 0;
+    if (exact_diag) {
+      rows_norms_diag(sk, sq, dq, p.l2norm != 0, scale, l, rkn, rqn, sDiag + RPW * w);
+    } else if (p.l2norm) {
+      rows_rsqrt(sk, rkn);
+      rows_rsqrt(sq, rqn);
+    } else {
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) rkn[r] = rqn[r] = 1.f;
+    }
     lds_barrier();
     // (beta V)^T, after the barrier: the region held the previous chunk's
     // output staging, read before it
@@ -1787,15 +1810,15 @@ __global__ __launch_bounds__(256, 2) void chunk_prefill_2wg_kernel(Params p) {
               f32x4 d;
 #pragma unroll
               for (int e = 0; e < 4; ++e) d[e] = 4 * lg + e > lr ? akk[m][e] : 0.f;
-              *reinterpret_cast<f32x4*>(sAd + bi[m] * AD_B + lr * 16 + 4 * lg) = d;
+              *reinterpret_cast<f32x4*>(sAd + ad_pos(bi[m], 4 * lg, lr)) = d;
             }
             // A_qk row 16bi + lr, columns 16bj + 4lg + e: kpos 8lg + 4(bj & 1) + e of 32-block bj >> 1;
             // the fp32 diagonal from sDiag
             const int i = 16 * bi[m] + lr, j0 = 16 * bj[m] + 4 * lg;
             f32x4 a;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) a[e] = i > j0 + e ? aqk[m][e] : 0.f;
-            if (bi[m] == bj[m] && (lr >> 2) == lg) a[lr & 3] = sDiag[i];
+            for (int e = 0; e < 4; ++e) a[e] = i >= j0 + e ? aqk[m][e] : 0.f;
+            if (exact_diag && bi[m] == bj[m] && (lr >> 2) == lg) a[lr & 3] = sDiag[i];
             *reinterpret_cast<bf16x4*>(sAqk + aqk_pos(bj[m] >> 1, bi[m], lr, 8 * lg + 4 * (bj[m] & 1))) =
                 to_bf16x4(a[0], a[1], a[2], a[3]);
           }
@@ -1830,19 +1853,19 @@ __global__ __launch_bounds__(256, 2) void chunk_prefill_2wg_kernel(Params p) {
         const int bb = l >> 4;
         int col = l & 15;
         asm volatile("" : "+v"(col));
-        const f32x4* Ab = reinterpret_cast<const f32x4*>(sAd + bb * AD_B);
+        const float* Ab = sAd + bb * AD_B;
         float x[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) x[i] = (i == col) ? 1.f : 0.f;
         f32x4 cur[4], nxt[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) cur[q] = Ab[q];
+        for (int q = 0; q < 4; ++q) cur[q] = *reinterpret_cast<const f32x4*>(Ab + ad_pos(0, 4 * q, 0));
 #pragma unroll
         for (int j = 0; j < 15; ++j) {
           if (j < 14) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-              if (4 * q + 3 > j + 1) nxt[q] = Ab[(j + 1) * 4 + q];
+              if (4 * q + 3 > j + 1) nxt[q] = *reinterpret_cast<const f32x4*>(Ab + ad_pos(0, 4 * q, j + 1));
           }
 #pragma unroll
           for (int i = j + 1; i < 16; ++i) x[i] -= cur[i >> 2][i & 3] * x[j];
