@@ -49,6 +49,10 @@
 //    ranks the sequences by length) so the long serial chains start early, and
 //    the V-block siblings of one (sequence, head) land on the same XCD so the
 //    shared q/k/g tiles are served from one L2.
+//  * Batches of many chains with K = V = 128 and bf16 q/k/v run a 4-wave
+//    variant in 80 KiB of LDS (chunk_prefill_2wg_kernel), so that two chains
+//    share each CU and the phases of one fill the idle issue slots of the
+//    other.
 #include "internal.h"
 
 #include <mutex>
