@@ -1618,14 +1618,23 @@ __global__ __launch_bounds__(256, 2) void chunk_prefill_2wg_kernel(Params p) {
       }
     }
     float gx[RPW][2], bt[RPW];
-    unsigned bvp[RPW];  // beta v of this lane's two value columns, a bf16 pair
+    // beta v of this lane's two value columns, packed as bf16 pairs of
+    // consecutive rows of one column (the layout of the transposed tile)
+    unsigned bvc[2][RPW / 2];
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       bt[r] = __uint_as_float(kBetaBF16 ? rb_[r] << 16 : rb_[r]);
       gx[r][0] = rg_[r][0];
       gx[r][1] = rg_[r][1];
-      bvp[r] = __builtin_bit_cast(unsigned, bf16x2{(__bf16)(bt[r] * __uint_as_float(rv_[r] << 16)),
-                                                   (__bf16)(bt[r] * __uint_as_float(rv_[r] & 0xffff0000u))});
+    }
+#pragma unroll
+    for (int r = 0; r < RPW; r += 2) {
+#pragma unroll
+      for (int vv = 0; vv < 2; ++vv) {
+        const float v0 = __uint_as_float(vv ? rv_[r] & 0xffff0000u : rv_[r] << 16);
+        const float v1 = __uint_as_float(vv ? rv_[r + 1] & 0xffff0000u : rv_[r + 1] << 16);
+        bvc[vv][r / 2] = __builtin_bit_cast(unsigned, bf16x2{(__bf16)(bt[r] * v0), (__bf16)(bt[r + 1] * v1)});
+      }
     }
     float sk[RPW], sq[RPW], dq[RPW];
 #pragma unroll
@@ -1667,15 +1676,8 @@ __global__ __launch_bounds__(256, 2) void chunk_prefill_2wg_kernel(Params p) {
 #pragma unroll
     for (int vv = 0; vv < 2; ++vv) {
 #pragma unroll
-      for (int j = 0; j < RPW / 4; ++j) {
-        bf16x4 x;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const unsigned u = bvp[4 * j + e];
-          x[e] = __builtin_bit_cast(__bf16, (unsigned short)(vv ? u >> 16 : u & 0xffffu));
-        }
-        *reinterpret_cast<bf16x4*>(sVT + tu_pos(c_lo + vv, RPW * w + 4 * j)) = x;
-      }
+      for (int j = 0; j < RPW / 4; ++j)
+        *reinterpret_cast<uint2*>(sVT + tu_pos(c_lo + vv, RPW * w + 4 * j)) = uint2{bvc[vv][2 * j], bvc[vv][2 * j + 1]};
     }
 
     // gamma in log2 units relative to the reference row m, the range guard
@@ -1713,8 +1715,11 @@ __global__ __launch_bounds__(256, 2) void chunk_prefill_2wg_kernel(Params p) {
     if (l == 0) sRed[w] = guard;
 
     // ---------------- phase A: KL, KR, QL; KE, KB, Qg kept as bf16 pairs ----
-    unsigned kep[RPW], kbp[RPW], qgp[RPW];
+    // KE and KB as bf16 pairs of consecutive rows of one channel (the layout
+    // of their transposed tiles), Qg as pairs of this lane's two channels
+    unsigned kec[2][RPW / 2], kbc[2][RPW / 2], qgp[RPW];
     {
+      float pke[2], pkb[2];  // the even row's values, packed with the odd row's
       float cg[2], cb[2];
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
@@ -1742,12 +1747,24 @@ __global__ __launch_bounds__(256, 2) void chunk_prefill_2wg_kernel(Params p) {
         *reinterpret_cast<bf16x2*>(sKL + rs_pos(i, c_lo)) = bf16x2{(__bf16)fkl[0], (__bf16)fkl[1]};
         *reinterpret_cast<bf16x2*>(sKR + rs_pos(i, c_lo)) = bf16x2{(__bf16)fkr[0], (__bf16)fkr[1]};
         *reinterpret_cast<bf16x2*>(sQL + rs_pos(i, c_lo)) = bf16x2{(__bf16)fql[0], (__bf16)fql[1]};
-        kep[r] = __builtin_bit_cast(unsigned, bf16x2{(__bf16)(fkl[0] * cg[0]), (__bf16)(fkl[1] * cg[1])});
-        kbp[r] = __builtin_bit_cast(unsigned, bf16x2{(__bf16)(fkr[0] * cb[0]), (__bf16)(fkr[1] * cb[1])});
         qgp[r] = __builtin_bit_cast(unsigned, bf16x2{(__bf16)(fql[0] * cg[0]), (__bf16)(fql[1] * cg[1])});
-        // packed here: left to itself the compiler keeps the six fp32
-        // products live through phase B and converts them at their stores
-        asm volatile("" : "+v"(kep[r]), "+v"(kbp[r]), "+v"(qgp[r]));
+        // packed here: left to itself the compiler keeps the fp32 products
+        // live through phase B and converts them at their stores
+        asm volatile("" : "+v"(qgp[r]));
+        if (r & 1) {
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) {
+            kec[cc][r / 2] = __builtin_bit_cast(unsigned, bf16x2{(__bf16)pke[cc], (__bf16)(fkl[cc] * cg[cc])});
+            kbc[cc][r / 2] = __builtin_bit_cast(unsigned, bf16x2{(__bf16)pkb[cc], (__bf16)(fkr[cc] * cb[cc])});
+            asm volatile("" : "+v"(kec[cc][r / 2]), "+v"(kbc[cc][r / 2]));
+          }
+        } else {
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) {
+            pke[cc] = fkl[cc] * cg[cc];
+            pkb[cc] = fkr[cc] * cb[cc];
+          }
+        }
       }
     }
     lds_barrier();
@@ -1841,15 +1858,8 @@ __global__ __launch_bounds__(256, 2) void chunk_prefill_2wg_kernel(Params p) {
       for (int cc = 0; cc < 2; ++cc) {
 #pragma unroll
         for (int j = 0; j < RPW / 4; ++j) {
-          bf16x4 xe, xb;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const unsigned ue = kep[4 * j + e], ub = kbp[4 * j + e];
-            xe[e] = __builtin_bit_cast(__bf16, (unsigned short)(cc ? ue >> 16 : ue & 0xffffu));
-            xb[e] = __builtin_bit_cast(__bf16, (unsigned short)(cc ? ub >> 16 : ub & 0xffffu));
-          }
-          *reinterpret_cast<bf16x4*>(sKE + tu_pos(c_lo + cc, RPW * w + 4 * j)) = xe;
-          *reinterpret_cast<bf16x4*>(sKB + kb_pos(c_lo + cc, RPW * w + 4 * j)) = xb;
+          *reinterpret_cast<uint2*>(sKE + tu_pos(c_lo + cc, RPW * w + 4 * j)) = uint2{kec[cc][2 * j], kec[cc][2 * j + 1]};
+          *reinterpret_cast<uint2*>(sKB + kb_pos(c_lo + cc, RPW * w + 4 * j)) = uint2{kbc[cc][2 * j], kbc[cc][2 * j + 1]};
         }
       }
       if (w == 0) {
@@ -1904,28 +1914,41 @@ __global__ __launch_bounds__(256, 2) void chunk_prefill_2wg_kernel(Params p) {
           }
         }
         __builtin_amdgcn_sched_barrier(0);
+        // the bf16 identity as an A operand (lane: row lr, columns 4lg..4lg+3):
+        // an MFMA with it widens a right-hand side to the C layout in fp32
+        // exactly, on the matrix cores instead of four VALU conversions
+        s16x4 ident;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ident[e] = (short)(lr == 4 * lg + e ? 0x3f80 : 0);
         s16x4 xb[4][4];
 #pragma unroll
         for (int bk = 0; bk < 4; ++bk) {
-          f32x4 acc[4];
+          s16x4 r[4];
+          if (bk == 0) {  // R_0 as loaded: bf16 already
 #pragma unroll
-          for (int m = 0; m < 4; ++m)
-            acc[m] = f32x4{(float)rb[m][bk][0], (float)rb[m][bk][1], (float)rb[m][bk][2], (float)rb[m][bk][3]};
+            for (int m = 0; m < 4; ++m) r[m] = __builtin_bit_cast(s16x4, rb[m][0]);
+          } else {
+            f32x4 acc[4];
 #pragma unroll
-          for (int c = 0; c < bk; ++c) {
+            for (int m = 0; m < 4; ++m)
+              acc[m] = mfma16(ident, __builtin_bit_cast(s16x4, rb[m][bk]), f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-            for (int m = 0; m < 4; ++m) acc[m] = mfma16(ab[bk][c], xb[m][c], acc[m]);
+            for (int c = 0; c < bk; ++c) {
+#pragma unroll
+              for (int m = 0; m < 4; ++m) acc[m] = mfma16(ab[bk][c], xb[m][c], acc[m]);
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) r[m] = pack4(acc[m]);
           }
           const s16x4 d = ab[bk][bk];
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
-            const s16x4 r = pack4(acc[m]);
-            const f32x4 x = mfma16(d, r, f32x4{0.f, 0.f, 0.f, 0.f});
+            const f32x4 x = mfma16(d, r[m], f32x4{0.f, 0.f, 0.f, 0.f});
             if (bk < 3) xb[m][bk] = pack4(x);
             if (m >= 2) {
               U[m - 2][bk] = x;
             } else {
-              const f32x4 xt = mfma16(r, d, f32x4{0.f, 0.f, 0.f, 0.f});
+              const f32x4 xt = mfma16(r[m], d, f32x4{0.f, 0.f, 0.f, 0.f});
               *reinterpret_cast<bf16x4*>(sKE + 2048 * w + w_pos(16 * bk + lr, 8 * lg + 4 * m)) =
                   to_bf16x4(-xt[0], -xt[1], -xt[2], -xt[3]);
             }
