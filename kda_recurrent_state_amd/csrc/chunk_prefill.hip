@@ -1556,12 +1556,14 @@ __global__ __launch_bounds__(256, 2) void chunk_prefill_2wg_kernel(Params p) {
       else
         rb_[r] = ld_at<unsigned>(bp, 4 * ri);
       const uint32_t ek = ri * 128u + cl;
-      rk_[r] = ld_at<unsigned>(kp, 2 * ek);
-      rq_[r] = ld_at<unsigned>(qp, 2 * ek);
-      rv_[r] = ld_at<unsigned>(vp, 2 * ek);
-      const float2 fg = ld_at<float2>(gp, 4 * ek);
-      rg_[r][0] = fg.x;
-      rg_[r][1] = fg.y;
+      // read once: non-temporal (-1 % on the e2e batch, -1.5 % with 2048 chains)
+      rk_[r] = __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(kp + 2 * ek));
+      rq_[r] = __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(qp + 2 * ek));
+      rv_[r] = __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(vp + 2 * ek));
+      typedef float f32x2 __attribute__((ext_vector_type(2)));
+      const f32x2 fg = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(gp + 4 * ek));
+      rg_[r][0] = fg[0];
+      rg_[r][1] = fg[1];
     }
   };
 
@@ -2064,14 +2066,17 @@ __global__ __launch_bounds__(256, 2) void chunk_prefill_2wg_kernel(Params p) {
     if (!retry) {
       lds_barrier();
       {
-        // 32-bit lane offsets from the chain's output pointer
+        // 32-bit lane offsets from the chain's output pointer; written once,
+        // non-temporal
+        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
         const uint32_t row_b = Hu * 256;
 #pragma unroll
         for (int u0 = 0; u0 < kC * 16; u0 += NT) {
           const int u = u0 + tid_i;
           const int i = u >> 4, cv = u & 15;
           if ((uint32_t)i < L)
-            *reinterpret_cast<bf16x8*>(op + ((uint32_t)i * row_b + 16 * (uint32_t)cv)) = ld8(sO + rs_pos(i, 8 * cv));
+            __builtin_nontemporal_store(__builtin_bit_cast(u32x4, ld8(sO + rs_pos(i, 8 * cv))),
+                                        reinterpret_cast<u32x4*>(op + ((uint32_t)i * row_b + 16 * (uint32_t)cv)));
         }
       }
       // advance the chain's pointers past this chunk
