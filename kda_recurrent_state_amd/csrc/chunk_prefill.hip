@@ -612,13 +612,15 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
         const uint32_t ev = ri * (uint32_t)vstride + vs;  // element offset in v
         if (kBF16) {
           if (CPL == 2) {
-            raw.k[r][0] = ld_at<unsigned>(kb, 2 * ek);
-            raw.q[r][0] = ld_at<unsigned>(qb, 2 * ek);
+            // rows are read once: non-temporal loads (and stores of the outputs)
+            raw.k[r][0] = __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(kb + 2 * ek));
+            raw.q[r][0] = __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(qb + 2 * ek));
           } else {
             raw.k[r][0] = ld_at<unsigned short>(kb, 2 * ek);
             raw.q[r][0] = ld_at<unsigned short>(qb, 2 * ek);
           }
-          raw.v[r][0] = VPL == 2 ? ld_at<unsigned>(vb, 2 * ev) : (unsigned)ld_at<unsigned short>(vb, 2 * ev);
+          raw.v[r][0] = VPL == 2 ? __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(vb + 2 * ev))
+                                 : (unsigned)ld_at<unsigned short>(vb, 2 * ev);
         } else {
           if (CPL == 2) {
             const uint2 a = ld_at<uint2>(kb, 4 * ek), c = ld_at<uint2>(qb, 4 * ek);
@@ -636,9 +638,10 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
           }
         }
         if (CPL == 2) {
-          const float2 fg = ld_at<float2>(gb, 4 * ek);
-          raw.g[r][0] = fg.x;
-          raw.g[r][CPL - 1] = fg.y;
+          typedef float f32x2 __attribute__((ext_vector_type(2)));
+          const f32x2 fg = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(gb + 4 * ek));
+          raw.g[r][0] = fg[0];
+          raw.g[r][CPL - 1] = fg[1];
         } else {
           raw.g[r][0] = ld_at<float>(gb, 4 * ek);
         }
@@ -1317,12 +1320,14 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
       // offsets (H * V <= 2^22 keeps them below 2^31 bytes)
       char* const ob = static_cast<char*>(p.out) + (((bos + t0) * H + h) * V + v0) * 2;
       const uint32_t row_b = (uint32_t)(H * V) * 2;
+      typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
       for (int u0 = 0; u0 < kC * VPR; u0 += NT) {
         const int u = u0 + tid_l;
         const int i = u / VPR, cv = u - i * VPR;
         if (i < L && v0 + 8 * cv < V)
-          *reinterpret_cast<bf16x8*>(ob + ((uint32_t)i * row_b + 16 * (uint32_t)cv)) = ld8(sO + i * C::LDO + 8 * cv);
+          __builtin_nontemporal_store(__builtin_bit_cast(u32x4, ld8(sO + i * C::LDO + 8 * cv)),
+                                      reinterpret_cast<u32x4*>(ob + ((uint32_t)i * row_b + 16 * (uint32_t)cv)));
       }
     } else {
       const int64_t vb = v0 + 16 * w + 4 * lg;  // this lane's first output column
