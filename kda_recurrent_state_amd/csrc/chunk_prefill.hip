@@ -1793,84 +1793,68 @@ __global__ __launch_bounds__(256, 2) void chunk_prefill_2wg_kernel(Params p) {
       Lcap = L > 16 ? 16 : (L > 4 ? 4 : 1);
     } else {
       // ---------------- phase B: A_kk (fp32 diagonal / bf16 below) and A_qk ----
-      {
-        const int wr = (w + 2) & 3;  // the three-pair waves are 2 and 3 (wave 0 goes on to phase C)
-        auto pairs = [&](auto npc) __attribute__((always_inline)) {
-          constexpr int NP = decltype(npc)::value;
-          int bi[NP], bj[NP];
+      // The ten 16x16 block pairs (bi >= bj) in two steps: each wave first
+      // takes the diagonal pair of its own rows (A_kk's fp32 diagonal blocks
+      // are all phase C needs), then wave 0 inverts them (phase C) while waves
+      // 1-3 take the six pairs below the diagonal, two each.
+      auto pairs = [&](auto npc, auto pick) __attribute__((always_inline)) {
+        constexpr int NP = decltype(npc)::value;
+        int bi[NP], bj[NP];
+#pragma unroll
+        for (int m = 0; m < NP; ++m) pick(m, bi[m], bj[m]);
+        f32x4 akk[NP], aqk[NP];
+        bf16x8 oL[2][NP], oR[2][NP], oQ[2][NP];
+        auto fetch = [&](int ks, int bf) __attribute__((always_inline)) {
 #pragma unroll
           for (int m = 0; m < NP; ++m) {
-            const int pr = wr + m * NW;
-            bi[m] = pr >= 6 ? 3 : (pr >= 3 ? 2 : (pr >= 1 ? 1 : 0));
-            bj[m] = pr - (bi[m] * (bi[m] + 1)) / 2;
-          }
-          f32x4 akk[NP], aqk[NP];
-          bf16x8 oL[2][NP], oR[2][NP], oQ[2][NP];
-          auto fetch = [&](int ks, int bf) __attribute__((always_inline)) {
-#pragma unroll
-            for (int m = 0; m < NP; ++m) {
-              oR[bf][m] = ld8(sKR + rs_pos(16 * bj[m] + lr, 32 * ks + 8 * lg));
-              oL[bf][m] = ld8(sKL + rs_pos(16 * bi[m] + lr, 32 * ks + 8 * lg));
-              oQ[bf][m] = ld8(sQL + rs_pos(16 * bi[m] + lr, 32 * ks + 8 * lg));
-            }
-          };
-#pragma unroll
-          for (int m = 0; m < NP; ++m) {
-            akk[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-            aqk[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-          }
-          fetch(0, 0);
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            if (ks + 1 < KS) fetch(ks + 1, (ks + 1) & 1);
-#pragma unroll
-            for (int m = 0; m < NP; ++m) {
-              akk[m] = mfma(oL[ks & 1][m], oR[ks & 1][m], akk[m]);
-              aqk[m] = mfma(oR[ks & 1][m], oQ[ks & 1][m], aqk[m]);
-            }
-          }
-#pragma unroll
-          for (int m = 0; m < NP; ++m) {
-            if (bi[m] != bj[m]) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) sAb[ab_pos(bi[m], bj[m], 4 * lg + e, lr)] = (__bf16)(-akk[m][e]);
-            } else {  // rows 4lg..4lg+3 of column lr, fp32, one 16-byte store
-              f32x4 d;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) d[e] = 4 * lg + e > lr ? akk[m][e] : 0.f;
-              *reinterpret_cast<f32x4*>(sAd + ad_pos(bi[m], 4 * lg, lr)) = d;
-            }
-            // A_qk row 16bi + lr, columns 16bj + 4lg + e: kpos 8lg + 4(bj & 1) + e of 32-block bj >> 1;
-            // the fp32 diagonal from sDiag
-            const int i = 16 * bi[m] + lr, j0 = 16 * bj[m] + 4 * lg;
-            f32x4 a;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) a[e] = i >= j0 + e ? aqk[m][e] : 0.f;
-            if (exact_diag && bi[m] == bj[m] && (lr >> 2) == lg) a[lr & 3] = sDiag[i];
-            *reinterpret_cast<bf16x4*>(sAqk + aqk_pos(bj[m] >> 1, bi[m], lr, 8 * lg + 4 * (bj[m] & 1))) =
-                to_bf16x4(a[0], a[1], a[2], a[3]);
+            oR[bf][m] = ld8(sKR + rs_pos(16 * bj[m] + lr, 32 * ks + 8 * lg));
+            oL[bf][m] = ld8(sKL + rs_pos(16 * bi[m] + lr, 32 * ks + 8 * lg));
+            oQ[bf][m] = ld8(sQL + rs_pos(16 * bi[m] + lr, 32 * ks + 8 * lg));
           }
         };
-        if (wr < 2)
-          pairs(std::integral_constant<int, 3>{});
-        else
-          pairs(std::integral_constant<int, 2>{});
-      }
+#pragma unroll
+        for (int m = 0; m < NP; ++m) {
+          akk[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+          aqk[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        fetch(0, 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if (ks + 1 < KS) fetch(ks + 1, (ks + 1) & 1);
+#pragma unroll
+          for (int m = 0; m < NP; ++m) {
+            akk[m] = mfma(oL[ks & 1][m], oR[ks & 1][m], akk[m]);
+            aqk[m] = mfma(oR[ks & 1][m], oQ[ks & 1][m], aqk[m]);
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < NP; ++m) {
+          if (bi[m] != bj[m]) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sAb[ab_pos(bi[m], bj[m], 4 * lg + e, lr)] = (__bf16)(-akk[m][e]);
+          } else {  // rows 4lg..4lg+3 of column lr, fp32, one 16-byte store
+            f32x4 d;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) d[e] = 4 * lg + e > lr ? akk[m][e] : 0.f;
+            *reinterpret_cast<f32x4*>(sAd + ad_pos(bi[m], 4 * lg, lr)) = d;
+          }
+          // A_qk row 16bi + lr, columns 16bj + 4lg + e: kpos 8lg + 4(bj & 1) + e of 32-block bj >> 1;
+          // the fp32 diagonal from sDiag
+          const int i = 16 * bi[m] + lr, j0 = 16 * bj[m] + 4 * lg;
+          f32x4 a;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a[e] = i >= j0 + e ? aqk[m][e] : 0.f;
+          if (exact_diag && bi[m] == bj[m] && (lr >> 2) == lg) a[lr & 3] = sDiag[i];
+          *reinterpret_cast<bf16x4*>(sAqk + aqk_pos(bj[m] >> 1, bi[m], lr, 8 * lg + 4 * (bj[m] & 1))) =
+              to_bf16x4(a[0], a[1], a[2], a[3]);
+        }
+      };
+      pairs(std::integral_constant<int, 1>{}, [&](int, int& bi, int& bj) { bi = bj = w; });
       lds_barrier();
 
-      // ---------------- KE, KB, Qg over KL, KR, QL; phase C ------------------
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) *reinterpret_cast<unsigned*>(sQg + rs_pos(RPW * w + r, kpos(c_lo))) = qgp[r];
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-#pragma unroll
-        for (int j = 0; j < RPW / 4; ++j) {
-          *reinterpret_cast<uint2*>(sKE + tu_pos(c_lo + cc, RPW * w + 4 * j)) = uint2{kec[cc][2 * j], kec[cc][2 * j + 1]};
-          *reinterpret_cast<uint2*>(sKB + kb_pos(c_lo + cc, RPW * w + 4 * j)) = uint2{kbc[cc][2 * j], kbc[cc][2 * j + 1]};
-        }
-      }
+      // ---------------- phase C: D_b = (I + A_bb)^-1; the pairs below the diagonal --
       if (w == 0) {
-        // D_b = (I + A_bb)^-1 by fp32 forward substitution; lane = (block, column)
+        // fp32 forward substitution; lane = (block, column)
         const int bb = l >> 4;
         int col = l & 15;
         asm volatile("" : "+v"(col));
@@ -1896,6 +1880,26 @@ __global__ __launch_bounds__(256, 2) void chunk_prefill_2wg_kernel(Params p) {
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) sAb[ab_pos(bb, bb, i, col)] = (__bf16)x[i];
+      } else {
+        // wave w: entries 2(w - 1) and 2w - 1 of (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+        pairs(std::integral_constant<int, 2>{}, [&](int m, int& bi, int& bj) {
+          const int e = 2 * (w - 1) + m;
+          bi = e < 1 ? 1 : (e < 3 ? 2 : 3);
+          bj = e - ((bi - 1) * bi) / 2;
+        });
+      }
+      lds_barrier();
+
+      // ---------------- KE, KB, Qg over KL, KR, QL (phase B has read them) ----
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) *reinterpret_cast<unsigned*>(sQg + rs_pos(RPW * w + r, kpos(c_lo))) = qgp[r];
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+#pragma unroll
+        for (int j = 0; j < RPW / 4; ++j) {
+          *reinterpret_cast<uint2*>(sKE + tu_pos(c_lo + cc, RPW * w + 4 * j)) = uint2{kec[cc][2 * j], kec[cc][2 * j + 1]};
+          *reinterpret_cast<uint2*>(sKB + kb_pos(c_lo + cc, RPW * w + 4 * j)) = uint2{kbc[cc][2 * j], kbc[cc][2 * j + 1]};
+        }
       }
       lds_barrier();
 
