@@ -1017,85 +1017,81 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     }
 
     // ---------------- phase B: A_kk (fp32) and A_qk (bf16) -----------------
-    // 10 lower 16x16 block pairs (bi >= bj), round-robin over waves; A_kk and
-    // A_qk of a pair share the key operand, and a wave's pairs run as
-    // interleaved independent accumulator chains.  A_qk is taken transposed
-    // (K Q^T) so that each lane holds four consecutive columns of one row.
-    // The pair count is uniform per wave, so each count has its own
-    // branch-free body whose operand reads run one contraction step ahead.
-    {
-      // rotated so that the extra pairs go to the waves that load after phase B
-      const int wr = w < NW / 2 ? w + NW / 2 : w - NW / 2;
-      auto pairs = [&](auto npc) {
-        constexpr int NP = decltype(npc)::value;
-        int bi[NP], bj[NP];
+    // The ten lower 16x16 block pairs (bi >= bj) in two steps.  Step 1: waves
+    // 0-3 take the diagonal pair of block w (A_kk's fp32 diagonal blocks are
+    // all phase C needs), waves 4.. the first pairs below the diagonal.  Step
+    // 2: wave 0 inverts the diagonal blocks (phase C) while other waves take
+    // the remaining pairs.  A_kk and A_qk of a pair share the key operand,
+    // and a wave's pairs run as interleaved independent accumulator chains.
+    // A_qk is taken transposed (K Q^T) so that each lane holds four
+    // consecutive columns of one row.  The pairs below the diagonal are
+    // numbered e = 0..5: (1,0) (2,0) (2,1) (3,0) (3,1) (3,2).
+    auto pairs = [&](auto npc, auto pick) {
+      constexpr int NP = decltype(npc)::value;
+      int bi[NP], bj[NP];
+#pragma unroll
+      for (int m = 0; m < NP; ++m) pick(m, bi[m], bj[m]);
+      f32x4 akk[NP], aqk[NP];
+      bf16x8 oL[2][NP], oR[2][NP], oQ[2][NP];
+      auto fetch = [&](int ks, int bf) {
 #pragma unroll
         for (int m = 0; m < NP; ++m) {
-          const int pr = wr + m * NW;
-          bi[m] = pr >= 6 ? 3 : (pr >= 3 ? 2 : (pr >= 1 ? 1 : 0));
-          bj[m] = pr - (bi[m] * (bi[m] + 1)) / 2;
-        }
-        f32x4 akk[NP], aqk[NP];
-        bf16x8 oL[2][NP], oR[2][NP], oQ[2][NP];
-        auto fetch = [&](int ks, int bf) {
-#pragma unroll
-          for (int m = 0; m < NP; ++m) {
-            oR[bf][m] = ld8(sKR + (16 * bj[m] + lr) * C::LDK + 32 * ks + 8 * lg);
-            oL[bf][m] = ld8(sKL + (16 * bi[m] + lr) * C::LDK + 32 * ks + 8 * lg);
-            if constexpr (kOut) oQ[bf][m] = ld8(sQL + (16 * bi[m] + lr) * C::LDK + 32 * ks + 8 * lg);
-          }
-        };
-#pragma unroll
-        for (int m = 0; m < NP; ++m) {
-          akk[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-          aqk[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        fetch(0, 0);
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-          if (ks + 1 < C::KS) fetch(ks + 1, (ks + 1) & 1);
-#pragma unroll
-          for (int m = 0; m < NP; ++m) {
-            akk[m] = mfma(oL[ks & 1][m], oR[ks & 1][m], akk[m]);
-            if constexpr (kOut) aqk[m] = mfma(oR[ks & 1][m], oQ[ks & 1][m], aqk[m]);
-          }
-        }
-#pragma unroll
-        for (int m = 0; m < NP; ++m) {
-          const int col = 16 * bj[m] + lr;
-          if (bi[m] != bj[m]) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sAb[(16 * bi[m] + 4 * lg + e) * C::LDT + col] = (__bf16)(-akk[m][e]);
-          } else {  // rows 4lg..4lg+3 of column lr: one 16-byte store
-            f32x4 d;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) d[e] = 4 * lg + e > lr ? akk[m][e] : 0.f;
-            *reinterpret_cast<f32x4*>(sAd + bi[m] * C::AD_B + lr * C::AD_C + 4 * lg) = d;
-          }
-          if constexpr (kOut) {  // row 16bi + lr, columns 16bj + 4lg + e; the fp32 diagonal from sDiag
-            const int i = 16 * bi[m] + lr, j0 = 16 * bj[m] + 4 * lg;
-            f32x4 a;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) a[e] = i >= j0 + e ? aqk[m][e] : 0.f;
-            if (exact_diag && bi[m] == bj[m] && (lr >> 2) == lg) a[lr & 3] = sDiag[i];
-            *reinterpret_cast<bf16x4*>(sAqk + i * C::LDA + kpos(j0)) = to_bf16x4(a[0], a[1], a[2], a[3]);
-          }
+          oR[bf][m] = ld8(sKR + (16 * bj[m] + lr) * C::LDK + 32 * ks + 8 * lg);
+          oL[bf][m] = ld8(sKL + (16 * bi[m] + lr) * C::LDK + 32 * ks + 8 * lg);
+          if constexpr (kOut) oQ[bf][m] = ld8(sQL + (16 * bi[m] + lr) * C::LDK + 32 * ks + 8 * lg);
         }
       };
-      constexpr int MP = (10 + NW - 1) / NW;  // pairs per wave at most
-      static_assert(MP >= 2 && MP <= 3, "pairs per wave");
-      const int np = (10 - wr + NW - 1) / NW;  // this wave's pairs (uniform)
-      if (np == MP)
-        pairs(std::integral_constant<int, MP>{});
-      else
-        pairs(std::integral_constant<int, MP - 1>{});
-    }
+#pragma unroll
+      for (int m = 0; m < NP; ++m) {
+        akk[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        aqk[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      fetch(0, 0);
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        if (ks + 1 < C::KS) fetch(ks + 1, (ks + 1) & 1);
+#pragma unroll
+        for (int m = 0; m < NP; ++m) {
+          akk[m] = mfma(oL[ks & 1][m], oR[ks & 1][m], akk[m]);
+          if constexpr (kOut) aqk[m] = mfma(oR[ks & 1][m], oQ[ks & 1][m], aqk[m]);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < NP; ++m) {
+        const int col = 16 * bj[m] + lr;
+        if (bi[m] != bj[m]) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sAb[(16 * bi[m] + 4 * lg + e) * C::LDT + col] = (__bf16)(-akk[m][e]);
+        } else {  // rows 4lg..4lg+3 of column lr: one 16-byte store
+          f32x4 d;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) d[e] = 4 * lg + e > lr ? akk[m][e] : 0.f;
+          *reinterpret_cast<f32x4*>(sAd + bi[m] * C::AD_B + lr * C::AD_C + 4 * lg) = d;
+        }
+        if constexpr (kOut) {  // row 16bi + lr, columns 16bj + 4lg + e; the fp32 diagonal from sDiag
+          const int i = 16 * bi[m] + lr, j0 = 16 * bj[m] + 4 * lg;
+          f32x4 a;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a[e] = i >= j0 + e ? aqk[m][e] : 0.f;
+          if (exact_diag && bi[m] == bj[m] && (lr >> 2) == lg) a[lr & 3] = sDiag[i];
+          *reinterpret_cast<bf16x4*>(sAqk + i * C::LDA + kpos(j0)) = to_bf16x4(a[0], a[1], a[2], a[3]);
+        }
+      }
+    };
+    // pair e below the diagonal: (bi, bj)
+    auto below = [](int e, int& bi, int& bj) {
+      bi = e < 1 ? 1 : (e < 3 ? 2 : 3);
+      bj = e - ((bi - 1) * bi) / 2;
+    };
+    if (w < 4)
+      pairs(std::integral_constant<int, 1>{}, [&](int, int& bi, int& bj) { bi = bj = w; });
+    else  // 8 waves: pairs 0-3 below the diagonal
+      pairs(std::integral_constant<int, 1>{}, [&](int, int& bi, int& bj) { below(w - 4, bi, bj); });
     lds_barrier();
 
-    // the other half's loads (they land while phases C-E compute)
-    if (!early && t0 + L < len) issue_loads(t0 + L, w);
-
     // ---------------- phase C: D_b = (I + A_bb)^-1 for the diagonal blocks --
+    // beside it, the pairs left below the diagonal: 8 waves, pairs 4 and 5 on
+    // waves 1 and 2; 4 waves, all six on waves 1-3, two each
     if (w == 0) {
       // fp32 forward substitution; lane = (block, column).  Step j needs
       // column j of the block: four 16-byte reads, issued one step ahead.
@@ -1124,7 +1120,13 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) sAb[(16 * bb + i) * C::LDT + 16 * bb + col] = (__bf16)x[i];
+    } else if constexpr (NW == 8) {
+      if (w < 3) pairs(std::integral_constant<int, 1>{}, [&](int, int& bi, int& bj) { below(w + 3, bi, bj); });
+    } else {
+      pairs(std::integral_constant<int, 2>{}, [&](int m, int& bi, int& bj) { below(2 * (w - 1) + m, bi, bj); });
     }
+    // the other half's loads (they land while phases D-E compute)
+    if (!early && t0 + L < len) issue_loads(t0 + L, w);
     lds_barrier();
 
     // ---------------- phase D: [W | U] = (I + A_kk)^-1 [beta K 2^gamma | beta V] --
