@@ -996,7 +996,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
     // The next chunk's loads: the first half of the waves (which the SIMD
     // arbiter favours, so they finish phase A first) issue theirs now, while
     // their SIMD partners finish phase A; the other half issue theirs after
-    // phase B, while wave 0 computes phase C.
+    // phase B's first step, while wave 0 computes phase C.
     const bool early = w < NW / 2;
     if (early && t0 + L < len) issue_loads(t0 + L, w);
     lds_barrier();
@@ -1913,6 +1913,9 @@ __global__ __launch_bounds__(256, 2) void chunk_prefill_2wg_kernel(Params p) {
       // holds four consecutive channels of one token, and stored as -W at once
       // over this wave's own pair of beta K 2^gamma (all of it read up front).
       f32x4 U[2][4];
+      // O^T = S^T Qg^T + V_new^T A_qk^T, its first term here: it needs only Qg
+      // and this wave's S, and its MFMAs fill the gaps of the dependent chain
+      f32x4 O[2][4];
       {
         s16x4 ab[4][4];
         bf16x4 rb[4][4];
@@ -1968,6 +1971,23 @@ __global__ __launch_bounds__(256, 2) void chunk_prefill_2wg_kernel(Params p) {
           }
         }
       }
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) O[m][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        bf16x8 aq[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) aq[rt] = ld8(sQg + rs_pos(16 * rt + lr, 32 * ks + 8 * lg));
+        const bf16x8 b0 = pack_perm(S[0][2 * ks], S[0][2 * ks + 1]);
+        const bf16x8 b1 = pack_perm(S[1][2 * ks], S[1][2 * ks + 1]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          O[0][rt] = mfma(b0, aq[rt], O[0][rt]);
+          O[1][rt] = mfma(b1, aq[rt], O[1][rt]);
+        }
+      }
       lds_barrier();
 
       // ---------------- phase E: the serial chain on this wave's 32 columns ----
@@ -1978,26 +1998,15 @@ __global__ __launch_bounds__(256, 2) void chunk_prefill_2wg_kernel(Params p) {
       // with S run together, one contraction step at a time, the next step's
       // W and Qg operands read ahead.
       f32x4 (&Vn)[2][4] = U;
-      f32x4 O[2][4];
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) O[m][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
       {
-        bf16x8 aw[2][4], aq[2][4];
+        bf16x8 aw[2][4];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          aw[0][rt] = ld8(sKE + w_pos(16 * rt + lr, 8 * lg));
-          aq[0][rt] = ld8(sQg + rs_pos(16 * rt + lr, 8 * lg));
-        }
+        for (int rt = 0; rt < 4; ++rt) aw[0][rt] = ld8(sKE + w_pos(16 * rt + lr, 8 * lg));
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           if (ks + 1 < KS) {
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-              aw[(ks + 1) & 1][rt] = ld8(sKE + 2048 * (ks + 1) + w_pos(16 * rt + lr, 8 * lg));
-              aq[(ks + 1) & 1][rt] = ld8(sQg + rs_pos(16 * rt + lr, 32 * (ks + 1) + 8 * lg));
-            }
+            for (int rt = 0; rt < 4; ++rt) aw[(ks + 1) & 1][rt] = ld8(sKE + 2048 * (ks + 1) + w_pos(16 * rt + lr, 8 * lg));
           }
           const bf16x8 b0 = pack_perm(S[0][2 * ks], S[0][2 * ks + 1]);
           const bf16x8 b1 = pack_perm(S[1][2 * ks], S[1][2 * ks + 1]);
@@ -2005,8 +2014,6 @@ __global__ __launch_bounds__(256, 2) void chunk_prefill_2wg_kernel(Params p) {
           for (int rt = 0; rt < 4; ++rt) {
             Vn[0][rt] = mfma(aw[ks & 1][rt], b0, Vn[0][rt]);
             Vn[1][rt] = mfma(aw[ks & 1][rt], b1, Vn[1][rt]);
-            O[0][rt] = mfma(b0, aq[ks & 1][rt], O[0][rt]);
-            O[1][rt] = mfma(b1, aq[ks & 1][rt], O[1][rt]);
           }
         }
       }
