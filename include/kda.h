@@ -226,10 +226,10 @@ kda_status_t kda_chunk_prefill(const kda_prefill_args_t* args, void* stream);
 
 /*
  * Bytes of device scratch that kda_chunk_prefill_noalloc keeps on each device
- * it runs on: 96 MiB, more than kda_chunk_prefill_workspace_size returns for
+ * it runs on: 256 MiB, more than kda_chunk_prefill_workspace_size returns for
  * any sizes kda_chunk_prefill accepts.
  */
-#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
 
 /*
  * kda_chunk_prefill_noalloc -- kda_chunk_prefill for callers that cannot

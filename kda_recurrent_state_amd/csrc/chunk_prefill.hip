@@ -382,17 +382,28 @@ struct Params {
   const int32_t* ckpt_cu;
   int64_t ckpt_iv, num_ckpt;
   int ckpt_bf16;
-  // segments: seq_of[n] is the sequence that work item n belongs to and
-  // seq_cu the sequences' token offsets (NULL: items are whole sequences)
+  // segments: seq_of[n] is the sequence that work item n belongs to, seq_cu
+  // the sequences' token offsets and seg_first[s] the first segment of
+  // sequence s (seq_of NULL: items are whole sequences).  seg_role picks the
+  // items of a pass and where their states come from and go:
+  //   kSegMaps  : the maps of the middle segments (neither first nor last of
+  //               their sequence; kOut = false)
+  //   kSegFirst : the first segment of each sequence, from the sequence's
+  //               initial state (row seq_of[n] of init): outputs, and its final
+  //               state to row n + 1 of sin_next (fp32), or to row seq_of[n] of
+  //               fin when it is also the last
+  //   kSegRest  : every other segment, from row n of init: outputs, the last
+  //               one of each sequence writing row seq_of[n] of fin
+  // Only segments below *seg_total are real.
   const int32_t* seq_of;
   const int32_t* seq_cu;
-  // with seq_of: skip_last = 1 for the map passes (the last segment of each
-  // sequence is skipped: its map is never composed); otherwise the last
-  // segment of each sequence writes that sequence's final state (row seq_of[n]
-  // of fin), and only segments below *seg_total are real
-  int skip_last;
+  const int32_t* seg_first;
+  int seg_role;
   const int32_t* seg_total;
+  float* sin_next;
 };
+
+constexpr int kSegMaps = 1, kSegFirst = 2, kSegRest = 3;
 
 // Raw bits of one chunk's inputs as loaded (bf16 pairs packed in one word, a
 // bf16 beta in the low half), kept in registers from the time the loads are
@@ -446,11 +457,10 @@ __device__ __forceinline__ void store_state(const f32x4 (&S)[KT], void* dst, int
 // are not computed.  Launched with BV == KP so that the K columns of M are
 // one 16-column tile per wave.
 template <int KP, int BV, bool kBF16, bool kOut>
-__global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
+__device__ __forceinline__ void chunk_body(const Params& p, char* smem) {
   using C = Cfg<KP, BV>;
   constexpr int NW = C::NW, NT = C::NT, RPW = C::RPW, CPL = C::CPL, VPL = C::VPL;
   static_assert(NT == BV * 4, "launch bounds");
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
   __bf16* sKL = reinterpret_cast<__bf16*>(smem + C::R_KL);
   __bf16* sQL = reinterpret_cast<__bf16*>(smem + C::R_QL);
   __bf16* sW = reinterpret_cast<__bf16*>(smem + C::R_QL);
@@ -494,18 +504,33 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
   const int64_t vcol = v0 + 16 * w + lr; // this lane's state column (state phase)
   const int64_t vcl = vcol < V ? vcol : V - 1;
   const int64_t srow = (n * H + h) * V;  // state row base of (n, h), in units of K elements
-  // final-state row and whether this item writes it (segments: see Params)
-  int64_t frow = srow;
+  // initial-state row, final-state destination and row, and whether this
+  // item writes it (segments: see Params)
+  int64_t irow = srow, frow = srow;
+  void* fdst = p.fin;
+  int fbf16 = p.fin_bf16;
   bool fin_ok = true;
   if (p.seq_of) {
     const int64_t sq = p.seq_of[n];
     int64_t se = p.seq_cu[sq + 1];
     se = se < 0 ? 0 : (se > p.T ? p.T : se);
-    const bool last = eos == se;
-    if (p.skip_last) {
-      if (last) return;
+    const bool last = eos == se, first = p.seg_first[sq] == n;
+    const bool real = n < (int64_t)*p.seg_total;
+    if (p.seg_role == kSegMaps) {
+      if (first || last) return;
+    } else if (p.seg_role == kSegFirst) {
+      if (!first || !real) return;
+      irow = (sq * H + h) * V;
+      if (last) {
+        frow = irow;
+      } else {
+        fdst = p.sin_next;
+        fbf16 = 0;
+        frow = srow + H * V;  // row n + 1
+      }
     } else {
-      fin_ok = last && n < (int64_t)*p.seg_total;
+      if (first) return;
+      fin_ok = last && real;
       frow = (sq * H + h) * V;
     }
   }
@@ -537,7 +562,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
       for (int ct = 0; ct < C::KT; ++ct) {
         const int64_t c0 = 16 * ct + 4 * lg;
         const int64_t cs = c0 < K ? c0 : K - 4;
-        const int64_t o = (srow + vcl) * K + cs;
+        const int64_t o = (irow + vcl) * K + cs;
         if (p.init_bf16) {
           const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const unsigned short*>(p.init) + o);
           S[ct] = f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
@@ -552,7 +577,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int64_t c = 16 * ct + 4 * lg + e;
-          const int64_t o = (srow + vcl) * K + (c < K ? c : K - 1);
+          const int64_t o = (irow + vcl) * K + (c < K ? c : K - 1);
           S[ct][e] = p.init_bf16 ? bf2f(static_cast<const unsigned short*>(p.init)[o])
                                  : static_cast<const float*>(p.init)[o];
         }
@@ -1363,10 +1388,37 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
   }
 
   // ---- final state ----
-  if (p.fin && fin_ok) store_state(S, p.fin, p.fin_bf16, p.svec, frow, lg, vcol, K, V);
+  if (fdst && fin_ok) store_state(S, fdst, fbf16, p.svec, frow, lg, vcol, K, V);
   if constexpr (!kOut) {
     if (map_m) store_state(SM, p.mmap, 0, p.svec, (n * H + h) * K, lg, (int64_t)mcol, K, K);
   }
+}
+
+template <int KP, int BV, bool kBF16, bool kOut>
+__global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
+  __shared__ __attribute__((aligned(16))) char smem[Cfg<KP, BV>::LDS];
+  chunk_body<KP, BV, kBF16, kOut>(p, smem);
+}
+
+// Pass 1 of the segment-parallel path in one launch: the first segment of
+// each sequence runs as an output item (pout, kSegFirst) and the middle
+// segments as map items (pmap, kSegMaps), side by side on the GPU.  Both
+// parameter sets describe the same segments and value blocks, so the
+// work-item mapping of chunk_body gives the same segment for a workgroup
+// under either.
+template <int KP, int BV, bool kBF16>
+__global__ __launch_bounds__(BV * 4) void chunk_prefill_seg1_kernel(Params pout, Params pmap) {
+  __shared__ __attribute__((aligned(16))) char smem[Cfg<KP, BV>::LDS];
+  const int64_t b = blockIdx.x;
+  const int64_t grp = b / (8 * pout.nvb);
+  const int64_t rem = b - grp * 8 * pout.nvb;
+  const int64_t item = grp * 8 + (rem & 7);
+  if (item >= pout.N * pout.H) return;
+  const int64_t n = item / pout.H;
+  if (pout.seg_first[pout.seq_of[n]] == n)
+    chunk_body<KP, BV, kBF16, true>(pout, smem);
+  else
+    chunk_body<KP, BV, kBF16, false>(pmap, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -2129,22 +2181,35 @@ __global__ __launch_bounds__(256, 2) void chunk_prefill_2wg_kernel(Params p) {
 }
 
 constexpr int64_t kPlanMaxN = 2048;
-constexpr int32_t kMinSplit = 3;  // fewest segments of the longest sequence worth the map passes
+
+// First-segment length for segments of lc tokens: a map chunk costs about
+// 0.8 of an output chunk (measured at K = V = 128, with both in one launch),
+// so a first segment of 0.8 lc tokens (its outputs, in pass 1) ends with the
+// middle segments' maps; a multiple of 64, at least 64.
+__host__ __device__ inline int64_t seg_first_len(int64_t lc) {
+  const int64_t l0 = (lc * 800 / 1000 + 32) / 64 * 64;
+  return l0 < 64 ? 64 : l0;
+}
 
 // ---------------------------------------------------------------------------
 // Segment-parallel prefill of long sequences.  When a batch has too few
-// (sequence, head) chains to fill the GPU, every sequence is cut into
-// segments of seg_len tokens.  A segment acts on the state as an affine map
-// F(S) = M S + b (maps compose in order; the composition is associative):
-//   pass 1 : every segment but the last of its sequence, in one pass: from a
-//            zero state -> b (its final state), and from the identity with
-//            zero values -> M (the same chunk operators act on both)
-//   scan   : S_in(first) = initial, S_in(next) = M S_in + b
-//   pass 2 : every segment again from its S_in -> outputs; the last segment
-//            of each sequence writes the sequence's final state
-// When the longest sequence would get fewer than kMinSplit segments, every
-// sequence is one segment: pass 1 then has nothing to do and pass 2 runs
-// whole sequences.
+// (sequence, head) chains to fill the GPU, every sequence is cut into a first
+// segment of l0 tokens and further segments of lc tokens.  A segment acts on
+// the state as an affine map F(S) = M S + b (maps compose in order; the
+// composition is associative):
+//   pass 1 : in one launch, side by side: the first segment of each sequence
+//            from the sequence's initial state -> its outputs and its final
+//            state (S_in of the second segment); and every middle segment
+//            (neither first nor last): from a zero state -> b, and from the
+//            identity with zero values -> M (the same chunk operators act on
+//            both)
+//   scan   : S_in(next) = M S_in + b from the second segment on
+//   pass 2 : every segment but the first from its S_in -> outputs; the last
+//            segment of each sequence writes the sequence's final state
+// A map chunk costs about l0 / lc (0.8) of an output chunk, so the first
+// segment's outputs end with the maps.  When splitting would not pay (the
+// planning kernel estimates both ways from the lengths), every sequence is
+// one segment and pass 1 runs whole sequences.
 // All segments of all sequences run in parallel in passes 1 and 2.
 // ---------------------------------------------------------------------------
 
@@ -2153,27 +2218,71 @@ constexpr int32_t kMinSplit = 3;  // fewest segments of the longest sequence wor
 // segment of sequence n, sfirst[N] the number of real segments; sseq[s] is
 // the sequence of segment s (0 for the empty ones).
 __global__ __launch_bounds__(1024) void seg_plan_kernel(const int32_t* __restrict__ cu, int64_t N, int64_t T,
-                                                        int64_t seg_len, int64_t nmax, int32_t* __restrict__ scu,
-                                                        int32_t* __restrict__ sfirst, int32_t* __restrict__ sseq) {
+                                                        int64_t H, int64_t lc_min, int64_t nmax,
+                                                        int32_t* __restrict__ scu, int32_t* __restrict__ sfirst,
+                                                        int32_t* __restrict__ sseq) {
   __shared__ int32_t cnt[1025], first[1025];
+  __shared__ int64_t lens[2];
+  if (threadIdx.x == 0) {
+    // lc: the smallest multiple of 64 from lc_min whose segments after the
+    // first make at most 256 pass-2 items (H per segment), by bisection (the
+    // count does not grow with lc); l0 = seg_first_len(lc)
+    auto items = [&](int64_t lc) {
+      const int64_t l0 = seg_first_len(lc);
+      int64_t c = 0;
+      for (int64_t n = 0; n < N; ++n) {
+        int64_t b0 = cu[n], e0 = cu[n + 1];
+        b0 = b0 < 0 ? 0 : (b0 > T ? T : b0);
+        e0 = e0 < b0 ? b0 : (e0 > T ? T : e0);
+        const int64_t len = e0 - b0;
+        c += len <= l0 ? 0 : (len - l0 + lc - 1) / lc;
+      }
+      return c * H;
+    };
+    int64_t lo = lc_min / 64, hi = (T + 63) / 64 + lo;  // items(64 hi) <= H N <= 256
+    while (lo < hi) {
+      const int64_t mid = (lo + hi) / 2;
+      if (items(64 * mid) <= 256) hi = mid; else lo = mid + 1;
+    }
+    lens[0] = seg_first_len(64 * lo);
+    lens[1] = 64 * lo;
+  }
+  __syncthreads();
+  const int64_t l0 = lens[0], lc = lens[1];
   for (int64_t n = threadIdx.x; n < N; n += blockDim.x) {
     int64_t b0 = cu[n], e0 = cu[n + 1];
     b0 = b0 < 0 ? 0 : (b0 > T ? T : b0);
     e0 = e0 < b0 ? b0 : (e0 > T ? T : e0);
-    const int64_t c = (e0 - b0 + seg_len - 1) / seg_len;
-    cnt[n] = (int32_t)(c > 1 ? c : 1);  // an empty sequence keeps one (empty) segment
+    // the first segment takes l0 tokens, the others lc; an empty sequence
+    // keeps one (empty) segment
+    const int64_t len = e0 - b0;
+    cnt[n] = (int32_t)(len <= l0 ? 1 : 1 + (len - l0 + lc - 1) / lc);
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    // Whole sequences when the longest would get fewer than kMinSplit
-    // segments: the map passes then cost more than the parallelism returns.
+    // Split only where it pays, in thousandths of one output chunk (64
+    // tokens): whole sequences take the longest one's chunks; split, pass 1
+    // takes max(l0, 0.825 lc) (the first segments' outputs beside the maps),
+    // pass 2 lc, the scan about 0.95 per composed map and the two extra
+    // launches about 6 (measured at K = V = 128, H = 32).
     int32_t cmax = 0;
-    for (int64_t n = 0; n < N; ++n) cmax = cnt[n] > cmax ? cnt[n] : cmax;
+    int64_t lmax = 0;
+    for (int64_t n = 0; n < N; ++n) {
+      cmax = cnt[n] > cmax ? cnt[n] : cmax;
+      int64_t b0 = cu[n], e0 = cu[n + 1];
+      b0 = b0 < 0 ? 0 : (b0 > T ? T : b0);
+      e0 = e0 < b0 ? b0 : (e0 > T ? T : e0);
+      lmax = e0 - b0 > lmax ? e0 - b0 : lmax;
+    }
+    const int64_t whole = 1000 * ((lmax + 63) / 64);
+    const int64_t p1 = cmax >= 3 ? (1000 * l0 > 825 * lc ? 1000 * l0 : 825 * lc) / 64 : 1000 * l0 / 64;
+    const int64_t split = p1 + 1000 * lc / 64 + (cmax >= 3 ? 950 * (cmax - 2) : 0) + 6000;
+    const bool seg = cmax >= 2 && split < whole;
     // prefix sums, clamped to nmax so that offsets that break the cu_seqlens
     // precondition still cannot index past the workspace
     int64_t run = 0;
     for (int64_t n = 0; n < N; ++n) {
-      const int64_t c = cmax < kMinSplit ? 1 : cnt[n];
+      const int64_t c = seg ? cnt[n] : 1;
       first[n] = (int32_t)run;
       run = run + c < nmax ? run + c : nmax;
     }
@@ -2186,7 +2295,7 @@ __global__ __launch_bounds__(1024) void seg_plan_kernel(const int32_t* __restric
     b0 = b0 < 0 ? 0 : (b0 > T ? T : b0);
     e0 = e0 < b0 ? b0 : (e0 > T ? T : e0);
     for (int64_t j = 0; first[n] + j < first[n + 1]; ++j) {
-      scu[first[n] + j] = (int32_t)(b0 + j * seg_len);
+      scu[first[n] + j] = (int32_t)(j == 0 ? b0 : b0 + l0 + (j - 1) * lc);
       sseq[first[n] + j] = (int32_t)n;
     }
   }
@@ -2198,10 +2307,11 @@ __global__ __launch_bounds__(1024) void seg_plan_kernel(const int32_t* __restric
 
 // Composes the segment maps of one (sequence, head) in fp32, for one block
 // of kScanCols value columns (the columns of S evolve independently under
-// S <- M S + b); 256 threads, K, V <= 128.  Writes each segment's initial
-// state S_in ([nmax, H, V, K] fp32) for these columns.  The last segment of a
-// sequence has no map (its pass-2 run writes the final state), so the
-// composition stops before it.
+// S <- M S + b); 256 threads, K, V <= 128.  Starts from the initial state of
+// the sequence's second segment (row sfirst[n] + 1 of S_in, [nmax, H, V, K]
+// fp32, written by pass 1) and writes those of the third segment on.  The
+// first segment has no map (pass 1 ran it from the true initial state) and
+// neither has the last (its pass-2 run writes the final state).
 //
 // The map of a segment is stored as the state that pass 1 propagated from
 // the identity: row x of the [K][K] tile holds M's column x, so
@@ -2216,9 +2326,8 @@ constexpr int kScanML = 128 + 4;                 // sT row stride
 constexpr int kScanV4 = 128 * 128 / 4 / kScanT;  // float4 of a 128 x 128 tile per thread
 
 __global__ __launch_bounds__(kScanT) void seg_scan_kernel(const int32_t* __restrict__ sfirst, const float* __restrict__ bmap,
-                                                          const float* __restrict__ mmap, const void* __restrict__ init,
-                                                          int init_bf16, float* __restrict__ sin, int64_t H, int64_t K,
-                                                          int64_t V) {
+                                                          const float* __restrict__ mmap, float* __restrict__ sin,
+                                                          int64_t H, int64_t K, int64_t V) {
   __shared__ __attribute__((aligned(16))) float sS[128 * kScanSL];  // S[c][v - v0]
   __shared__ __attribute__((aligned(16))) float sT[128 * kScanML];  // T[x][c]
   const int64_t ncb = (V + kScanCols - 1) / kScanCols;
@@ -2226,22 +2335,20 @@ __global__ __launch_bounds__(kScanT) void seg_scan_kernel(const int32_t* __restr
   const int64_t v0 = (blockIdx.x - item * ncb) * kScanCols;
   const int64_t n = item / H, h = item % H;
   const int tid = threadIdx.x;
-  const int64_t srow = (n * H + h) * V;  // [.., H, V, K] row base of (n, h)
+  // the maps of segments s0 .. s1 - 2 are composed (uniform)
+  const int64_t s0 = sfirst[n] + 1, s1 = sfirst[n + 1];
+  if (s0 + 1 >= s1) return;
   const bool vec = (K & 3) == 0;
   const int nv4 = (int)(K * K / 4);      // float4 of a K x K tile
   // coalesced element order: e -> (column vl, channel c), c fastest
   for (int e = tid; e < kScanCols * 128; e += kScanT) {
     const int c = e & 127, vl = e >> 7;
     float x = 0.f;
-    if (init && c < K && v0 + vl < V) {
-      const int64_t o = (srow + v0 + vl) * K + c;
-      x = init_bf16 ? bf2f(static_cast<const unsigned short*>(init)[o]) : static_cast<const float*>(init)[o];
-    }
+    if (c < K && v0 + vl < V) x = sin[((s0 * H + h) * V + v0 + vl) * K + c];
     sS[c * kScanSL + vl] = x;
   }
   const int r = tid >> 1;                      // this thread's state row (key channel)
   const int j0 = (tid & 1) * (kScanCols / 2);  // and its kScanCols / 2 columns
-  const int64_t s0 = sfirst[n], s1 = sfirst[n + 1];
   f32x4 tr[kScanV4];        // the next segment's T (vector path)
   float br[kScanCols / 2];  // and this thread's b entries
   auto fetch = [&](int64_t sg) {
@@ -2259,13 +2366,15 @@ __global__ __launch_bounds__(kScanT) void seg_scan_kernel(const int32_t* __restr
       br[j] = (r < K && v < V) ? bmap[((sg * H + h) * V + v) * K + r] : 0.f;
     }
   };
-  if (s0 + 1 < s1) fetch(s0);
+  fetch(s0);
   __syncthreads();
   for (int64_t sg = s0; sg < s1; ++sg) {
-    const int64_t srow_s = (sg * H + h) * V;
-    for (int e = tid; e < kScanCols * 128; e += kScanT) {
-      const int c = e & 127, vl = e >> 7;
-      if (v0 + vl < V && c < K) sin[(srow_s + v0 + vl) * K + c] = sS[c * kScanSL + vl];
+    if (sg > s0) {  // S_in of segment sg (that of s0 came from pass 1)
+      const int64_t srow_s = (sg * H + h) * V;
+      for (int e = tid; e < kScanCols * 128; e += kScanT) {
+        const int c = e & 127, vl = e >> 7;
+        if (v0 + vl < V && c < K) sin[(srow_s + v0 + vl) * K + c] = sS[c * kScanSL + vl];
+      }
     }
     if (sg + 1 == s1) break;  // uniform: the last segment's map is not composed
     if (vec) {
@@ -2335,7 +2444,7 @@ hipError_t launch_cfg(const Params& prm, bool bf16, hipStream_t stream) {
   }
   if constexpr (KP == 128 && BV == 128) {
     if (bf16 && prm.K == 128 && prm.V == 128 && prm.pair && prm.ovec && items >= kTwoPerCuMinChains &&
-        prm.T <= INT32_MAX && prm.H <= 65535) {
+        prm.T <= INT32_MAX && prm.H <= 65535 && !prm.seq_of) {
       if (prm.beta_bf16)
         hipLaunchKernelGGL(chunk_prefill_2wg_kernel<true>, dim3((unsigned)items), dim3(w2::NT), 0, stream, prm);
       else
@@ -2350,13 +2459,43 @@ hipError_t launch_cfg(const Params& prm, bool bf16, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Picks the kernel variant for these sizes and launches it.
-hipError_t launch_variant(Params prm, bool bf16, hipStream_t stream) {
+// Vector-access flags of a parameter set (from sizes and pointer alignment).
+void set_access_flags(Params& prm) {
   const uintptr_t al = (uintptr_t)prm.q | (uintptr_t)prm.k | (uintptr_t)prm.v | (uintptr_t)prm.g;
   prm.pair = (prm.K % 2 == 0) && (prm.V % 2 == 0) && (al % 8 == 0);
   prm.ovec = (prm.V % 8 == 0) && ((uintptr_t)prm.out % 16 == 0);
-  const uintptr_t sal = (uintptr_t)prm.init | (uintptr_t)prm.fin | (uintptr_t)prm.ckpt | (uintptr_t)prm.mmap;
+  const uintptr_t sal = (uintptr_t)prm.init | (uintptr_t)prm.fin | (uintptr_t)prm.ckpt | (uintptr_t)prm.mmap |
+                        (uintptr_t)prm.sin_next;
   prm.svec = (prm.K % 4 == 0) && (sal % 16 == 0);
+}
+
+// Pass 1 of the segment-parallel path (chunk_prefill_seg1_kernel): both roles
+// with the value blocks of the map pass (128 columns, 64 for K <= 64).
+hipError_t launch_seg1(Params pout, Params pmap, bool bf16, hipStream_t stream) {
+  set_access_flags(pout);
+  set_access_flags(pmap);
+  pmap.svec = pout.svec = pout.svec && pmap.svec;
+  const bool small = pout.K <= 64;
+  pout.nvb = pmap.nvb = (int)(small ? (pout.V + 63) / 64 : (pout.V + 127) / 128);
+  const int64_t grid = (pout.N * pout.H + 7) / 8 * 8 * pout.nvb;
+  const dim3 g3((unsigned)grid), b3(small ? 256 : 512);
+  if (small) {
+    if (bf16)
+      hipLaunchKernelGGL((chunk_prefill_seg1_kernel<64, 64, true>), g3, b3, 0, stream, pout, pmap);
+    else
+      hipLaunchKernelGGL((chunk_prefill_seg1_kernel<64, 64, false>), g3, b3, 0, stream, pout, pmap);
+  } else {
+    if (bf16)
+      hipLaunchKernelGGL((chunk_prefill_seg1_kernel<128, 128, true>), g3, b3, 0, stream, pout, pmap);
+    else
+      hipLaunchKernelGGL((chunk_prefill_seg1_kernel<128, 128, false>), g3, b3, 0, stream, pout, pmap);
+  }
+  return hipGetLastError();
+}
+
+// Picks the kernel variant for these sizes and launches it.
+hipError_t launch_variant(Params prm, bool bf16, hipStream_t stream) {
+  set_access_flags(prm);
   if (prm.K <= 64) {
     prm.nvb = (int)((prm.V + 63) / 64);
     return launch_cfg<64, 64>(prm, bf16, stream);
@@ -2377,12 +2516,16 @@ hipError_t launch_variant(Params prm, bool bf16, hipStream_t stream) {
   return launch_cfg<128, 128>(prm, bf16, stream);
 }
 
-// Segment length when a batch is cut into segments, 0 when it is not.
+// Smallest length of the segments after the first when a batch is cut into
+// segments, 0 when it is not: with a first segment of l0 = 0.8 lc tokens,
+// H (T - N l0) / lc = 256 pass-2 items gives lc = H T / (256 + 0.8 N H)
+// (the planning kernel may take longer segments, never shorter).
 int64_t segment_length(int64_t T, int64_t N, int64_t H, int64_t K, int64_t V) {
   if (N * H >= 256 || T < 16384 || K > 128 || V > 128 || N > 1024) return 0;
-  int64_t ls = (T * H + 255) / 256;  // about one chain per CU
-  ls = (ls + 63) / 64 * 64;
-  return ls < 2048 ? 2048 : ls;
+  const int64_t den = 256000 + 800 * N * H;
+  int64_t lc = (H * T * 1000 + den - 1) / den;
+  lc = (lc + 63) / 64 * 64;
+  return lc < 2048 ? 2048 : lc;
 }
 
 struct SegLayout {
@@ -2396,7 +2539,11 @@ SegLayout seg_layout(int64_t T, int64_t N, int64_t H, int64_t K, int64_t V) {
   SegLayout L;
   L.seg_len = segment_length(T, N, H, K, V);
   if (!L.seg_len) return L;
-  L.nmax = N + T / L.seg_len;
+  // a sequence of len > l0 tokens has 1 + ceil((len - l0) / lc) segments, at
+  // most 2 + (len - l0) / lc < 1.25 + len / lc (l0 >= 0.8 lc - 32, lc >=
+  // seg_len >= 2048; one segment when len <= l0): fewer than
+  // 1.25 N + T / seg_len + 1 in all
+  L.nmax = N + (4 * T + N * L.seg_len) / (4 * L.seg_len) + 1;
   size_t o = 0;
   L.off_scu = o;     o += round256(sizeof(int32_t) * (size_t)(L.nmax + 1));
   L.off_sfirst = o;  o += round256(sizeof(int32_t) * (size_t)(N + 1));
@@ -2447,8 +2594,10 @@ hipError_t launch_chunk_prefill(const kda_prefill_args_t& a, hipStream_t stream)
   prm.ckpt_bf16 = a.ckpt_dtype == KDA_BF16;
   prm.seq_of = nullptr;
   prm.seq_cu = nullptr;
-  prm.skip_last = 0;
+  prm.seg_first = nullptr;
+  prm.seg_role = 0;
   prm.seg_total = nullptr;
+  prm.sin_next = nullptr;
   const bool bf16 = a.qkv_dtype == KDA_BF16;
   hipError_t e;
 
@@ -2461,37 +2610,41 @@ hipError_t launch_chunk_prefill(const kda_prefill_args_t& a, hipStream_t stream)
     float* bmap = reinterpret_cast<float*>(ws + L.off_b);
     float* mmap = reinterpret_cast<float*>(ws + L.off_m);
     float* sin = reinterpret_cast<float*>(ws + L.off_sin);
-    hipLaunchKernelGGL(seg_plan_kernel, dim3(1), dim3(1024), 0, stream, a.cu_seqlens, a.N, a.T, L.seg_len, L.nmax,
-                       scu, sfirst, sseq);
+    hipLaunchKernelGGL(seg_plan_kernel, dim3(1), dim3(1024), 0, stream, a.cu_seqlens, a.N, a.T, a.H, L.seg_len,
+                       L.nmax, scu, sfirst, sseq);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     Params seg = prm;
     seg.cu = scu;
     seg.N = L.nmax;
-    // pass 1: the map (M, b) of every segment but the last of its sequence
-    Params p1 = seg;
-    p1.init = nullptr;
-    p1.out = nullptr;
-    p1.ckpt = nullptr;
-    p1.fin = bmap;
-    p1.fin_bf16 = 0;
-    p1.mmap = mmap;
-    p1.seq_of = sseq;
-    p1.seq_cu = a.cu_seqlens;
-    p1.skip_last = 1;
-    if ((e = launch_variant(p1, bf16, stream)) != hipSuccess) return e;
-    // scan: S_in of every segment, final states
+    seg.seq_of = sseq;
+    seg.seq_cu = a.cu_seqlens;
+    seg.seg_first = sfirst;
+    seg.seg_total = sfirst + a.N;
+    // pass 1: the first segments' outputs (from the sequences' initial
+    // states) beside the middle segments' maps (M, b)
+    Params pf = seg;
+    pf.seg_role = kSegFirst;
+    pf.sin_next = sin;
+    Params pm = seg;
+    pm.seg_role = kSegMaps;
+    pm.init = nullptr;
+    pm.out = nullptr;
+    pm.ckpt = nullptr;
+    pm.fin = bmap;
+    pm.fin_bf16 = 0;
+    pm.mmap = mmap;
+    if ((e = launch_seg1(pf, pm, bf16, stream)) != hipSuccess) return e;
+    // scan: S_in of every segment after the second
     const int64_t ncb = (a.V + kScanCols - 1) / kScanCols;
     hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)(a.N * a.H * ncb)), dim3(256), 0, stream, sfirst, bmap, mmap,
-                       a.initial_state, prm.init_bf16, sin, a.H, a.K, a.V);
+                       sin, a.H, a.K, a.V);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // pass 2: outputs of every segment from its true initial state
-    Params p3 = seg;
-    p3.init = sin;
-    p3.init_bf16 = 0;
-    p3.seq_of = sseq;
-    p3.seq_cu = a.cu_seqlens;
-    p3.seg_total = sfirst + a.N;
-    return launch_variant(p3, bf16, stream);
+    // pass 2: outputs of the other segments from their initial states
+    Params pr = seg;
+    pr.seg_role = kSegRest;
+    pr.init = sin;
+    pr.init_bf16 = 0;
+    return launch_variant(pr, bf16, stream);
   }
 
   if (a.N >= 2 && a.N <= kPlanMaxN) {

@@ -322,13 +322,14 @@ def _noalloc_max():
 def test_noalloc_scratch_covers_every_accepted_size(lib):
     """The static scratch of kda_chunk_prefill_noalloc holds the workspace of
     every size kda_chunk_prefill accepts.  The segment maps are the largest
-    part: with N*H < 256 chains the segment length is at least T*H/256, so a
-    batch has at most N*H + 256 (segment, head) maps of 3*K*V*4 bytes
-    (K, V <= 128 on that path) -- at most 511 * 192 KiB; the sequence-order
-    plan needs 4 bytes per sequence for N <= 2048."""
+    part: with N*H < 256 chains the segments after each sequence's first are
+    at least lc = H*T / (256 + 0.8*N*H) tokens long, so a batch has fewer than
+    1.25*N + T/lc + 1 segments, i.e. at most 2.05*N*H + 256 + H < 1040
+    (segment, head) slots of 3*K*V*4 bytes (K, V <= 128 on that path) --
+    195 MiB; the sequence-order plan needs 4 bytes per sequence for N <= 2048."""
     import numpy as np
     mx = _noalloc_max()
-    assert 511 * 3 * 128 * 128 * 4 + 64 * 1024 <= mx
+    assert 1040 * 3 * 128 * 128 * 4 + 64 * 1024 <= mx
     ts = sorted(set([int(x) for x in np.geomspace(16384, 1 << 26, 300)] + [2048 * k for k in range(8, 520)]))
     worst = 0
     for H in range(1, 256):
