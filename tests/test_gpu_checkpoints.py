@@ -90,7 +90,8 @@ def test_checkpoints_with_shortened_chunks():
     ([20000], 2, 64, 64, 640),
     ([20000], 2, 64, 64, 2048),
     ([17000, 100, 0], 4, 128, 128, 1024),
-    ([4096] * 4, 2, 64, 64, 1024),        # whole sequences (at most two segments each)
+    ([4096] * 4, 2, 64, 64, 1024),        # whole sequences (splitting would not pay)
+    ([17000, 5000, 3000, 100], 2, 64, 64, 1024),  # 9, 3, 2 and 1 segments
 ])
 def test_checkpoints_on_segmented_path(lengths, H, K, V, interval):
     import kda_recurrent_state_amd as kda

@@ -288,8 +288,12 @@ def test_deterministic(lengths, H):
     ([17000, 100, 0], 4, 128, 128, "bf16", True),
     ([9000, 9001], 3, 32, 48, "f32", True),
     ([17000], 2, 30, 50, "bf16", True),   # K not a multiple of 4: element loads in the map scan
-    ([4096] * 4, 2, 128, 128, "bf16", True),         # at most two segments each: whole sequences
+    ([4096] * 4, 2, 128, 128, "bf16", True),         # splitting would not pay: whole sequences
     ([4096, 0, 4096, 4096, 4096], 2, 64, 64, "f32", True),  # whole sequences and an empty one
+    # 9, 3, 2 and 1 segments: maps and a scan, one map, a first and a last
+    # segment only (no map), and a first segment that is also the last
+    ([17000, 5000, 3000, 100], 2, 64, 64, "bf16", True),
+    ([17000, 5000, 3000, 100], 2, 128, 128, "f32", False),
 ])
 def test_segmented_long_sequences(lengths, H, K, V, dtype, init):
     import kda_recurrent_state_amd as kda
@@ -301,11 +305,11 @@ def test_segmented_long_sequences(lengths, H, K, V, dtype, init):
 
 
 @pytest.mark.parametrize("lengths,H,K,V", [
-    ([131072], 2, 64, 64),     # 64 segments of 2048 tokens
-    ([131072], 1, 128, 128),   # 64 segments, 128-column value blocks
+    ([131072], 2, 64, 64),     # 65 segments (1664 tokens, then 2048)
+    ([131072], 1, 128, 128),   # the same with 128-column value blocks
 ])
 def test_many_segments_compose(lengths, H, K, V):
-    """64 segment maps composed in order: drift in the fp32 composition of
+    """63 segment maps composed in order: drift in the fp32 composition of
     maps built from bf16 operands would show up here first."""
     import kda_recurrent_state_amd as kda
     T = sum(lengths)
