@@ -456,7 +456,8 @@ __device__ __forceinline__ void store_state(const f32x4 (&S)[KT], void* dst, int
 // decays; its U is zero); q, the query tiles, A_qk and the output products
 // are not computed.  Launched with BV == KP so that the K columns of M are
 // one 16-column tile per wave.
-template <int KP, int BV, bool kBF16, bool kOut>
+// kSeg: the items are segments (p.seq_of set; segment passes only).
+template <int KP, int BV, bool kBF16, bool kOut, bool kSeg>
 __device__ __forceinline__ void chunk_body(const Params& p, char* smem) {
   using C = Cfg<KP, BV>;
   constexpr int NW = C::NW, NT = C::NT, RPW = C::RPW, CPL = C::CPL, VPL = C::VPL;
@@ -510,7 +511,7 @@ __device__ __forceinline__ void chunk_body(const Params& p, char* smem) {
   void* fdst = p.fin;
   int fbf16 = p.fin_bf16;
   bool fin_ok = true;
-  if (p.seq_of) {
+  if constexpr (kSeg) {
     const int64_t sq = p.seq_of[n];
     int64_t se = p.seq_cu[sq + 1];
     se = se < 0 ? 0 : (se > p.T ? p.T : se);
@@ -726,7 +727,7 @@ __device__ __forceinline__ void chunk_body(const Params& p, char* smem) {
   int64_t ck_next = INT64_MAX, ck_row = 0, ck_end = 0;
   if (p.ckpt) {
     int64_t seq = n, off = 0;
-    if (p.seq_of) {
+    if constexpr (kSeg) {
       seq = p.seq_of[n];
       int64_t sb = p.seq_cu[seq];
       sb = sb < 0 ? 0 : (sb > p.T ? p.T : sb);
@@ -1394,10 +1395,10 @@ __device__ __forceinline__ void chunk_body(const Params& p, char* smem) {
   }
 }
 
-template <int KP, int BV, bool kBF16, bool kOut>
+template <int KP, int BV, bool kBF16, bool kSeg>
 __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) char smem[Cfg<KP, BV>::LDS];
-  chunk_body<KP, BV, kBF16, kOut>(p, smem);
+  chunk_body<KP, BV, kBF16, true, kSeg>(p, smem);
 }
 
 // Pass 1 of the segment-parallel path in one launch: the first segment of
@@ -1416,9 +1417,9 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_seg1_kernel(Params pout,
   if (item >= pout.N * pout.H) return;
   const int64_t n = item / pout.H;
   if (pout.seg_first[pout.seq_of[n]] == n)
-    chunk_body<KP, BV, kBF16, true>(pout, smem);
+    chunk_body<KP, BV, kBF16, true, true>(pout, smem);
   else
-    chunk_body<KP, BV, kBF16, false>(pmap, smem);
+    chunk_body<KP, BV, kBF16, false, true>(pmap, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -2433,15 +2434,6 @@ hipError_t launch_cfg(const Params& prm, bool bf16, hipStream_t stream) {
   const int64_t grid = groups * 8 * prm.nvb;
   constexpr int nt = Cfg<KP, BV>::NT;
   const dim3 g3((unsigned)grid), b3(nt);
-  if constexpr (KP == BV) {
-    if (prm.mmap) {  // segment maps
-      if (bf16)
-        hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, true, false>), g3, b3, 0, stream, prm);
-      else
-        hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, false, false>), g3, b3, 0, stream, prm);
-      return hipGetLastError();
-    }
-  }
   if constexpr (KP == 128 && BV == 128) {
     if (bf16 && prm.K == 128 && prm.V == 128 && prm.pair && prm.ovec && items >= kTwoPerCuMinChains &&
         prm.T <= INT32_MAX && prm.H <= 65535 && !prm.seq_of) {
@@ -2452,10 +2444,17 @@ hipError_t launch_cfg(const Params& prm, bool bf16, hipStream_t stream) {
       return hipGetLastError();
     }
   }
-  if (bf16)
-    hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, true, true>), g3, b3, 0, stream, prm);
-  else
-    hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, false, true>), g3, b3, 0, stream, prm);
+  if (prm.seq_of) {
+    if (bf16)
+      hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, true, true>), g3, b3, 0, stream, prm);
+    else
+      hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, false, true>), g3, b3, 0, stream, prm);
+  } else {
+    if (bf16)
+      hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, true, false>), g3, b3, 0, stream, prm);
+    else
+      hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, false, false>), g3, b3, 0, stream, prm);
+  }
   return hipGetLastError();
 }
 
@@ -2499,10 +2498,6 @@ hipError_t launch_variant(Params prm, bool bf16, hipStream_t stream) {
   if (prm.K <= 64) {
     prm.nvb = (int)((prm.V + 63) / 64);
     return launch_cfg<64, 64>(prm, bf16, stream);
-  }
-  if (prm.mmap) {  // segment maps: the K columns of M need 128-column value blocks
-    prm.nvb = (int)((prm.V + 127) / 128);
-    return launch_cfg<128, 128>(prm, bf16, stream);
   }
   // 128-column value blocks whenever V allows, also for few (sequence, head)
   // chains: 64-column blocks double the workgroups, but each repeats the
