@@ -1128,21 +1128,22 @@ __device__ __forceinline__ void chunk_body(const Params& p, char* smem) {
       float x[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) x[i] = (i == col) ? 1.f : 0.f;
-      f32x4 cur[4], nxt[4];
+      // columns j + 1 and j + 2 in flight during step j (a ring of three)
+      f32x4 cr[3][4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) cur[q] = Ab[q];  // column 0
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cr[c][q] = Ab[c * (C::AD_C / 4) + q];
 #pragma unroll
       for (int j = 0; j < 15; ++j) {
-        if (j < 14) {
+        if (j + 2 < 15) {
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            if (4 * q + 3 > j + 1) nxt[q] = Ab[(j + 1) * (C::AD_C / 4) + q];
+            if (4 * q + 3 > j + 2) cr[(j + 2) % 3][q] = Ab[(j + 2) * (C::AD_C / 4) + q];
         }
 #pragma unroll
-        for (int i = j + 1; i < 16; ++i) x[i] -= cur[i >> 2][i & 3] * x[j];
-        __builtin_amdgcn_sched_barrier(0);  // one column in flight at a time (register pressure)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) cur[q] = nxt[q];
+        for (int i = j + 1; i < 16; ++i) x[i] -= cr[j % 3][i >> 2][i & 3] * x[j];
+        __builtin_amdgcn_sched_barrier(0);  // (register pressure)
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) sAb[(16 * bb + i) * C::LDT + 16 * bb + col] = (__bf16)x[i];
@@ -1917,21 +1918,22 @@ __global__ __launch_bounds__(256, 2) void chunk_prefill_2wg_kernel(Params p) {
         float x[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) x[i] = (i == col) ? 1.f : 0.f;
-        f32x4 cur[4], nxt[4];
+        // columns j + 1 and j + 2 in flight during step j (a ring of three)
+        f32x4 cr[3][4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) cur[q] = *reinterpret_cast<const f32x4*>(Ab + ad_pos(0, 4 * q, 0));
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) cr[c][q] = *reinterpret_cast<const f32x4*>(Ab + ad_pos(0, 4 * q, c));
 #pragma unroll
         for (int j = 0; j < 15; ++j) {
-          if (j < 14) {
+          if (j + 2 < 15) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-              if (4 * q + 3 > j + 1) nxt[q] = *reinterpret_cast<const f32x4*>(Ab + ad_pos(0, 4 * q, j + 1));
+              if (4 * q + 3 > j + 2) cr[(j + 2) % 3][q] = *reinterpret_cast<const f32x4*>(Ab + ad_pos(0, 4 * q, j + 2));
           }
 #pragma unroll
-          for (int i = j + 1; i < 16; ++i) x[i] -= cur[i >> 2][i & 3] * x[j];
+          for (int i = j + 1; i < 16; ++i) x[i] -= cr[j % 3][i >> 2][i & 3] * x[j];
           __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) cur[q] = nxt[q];
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) sAb[ab_pos(bb, bb, i, col)] = (__bf16)x[i];
