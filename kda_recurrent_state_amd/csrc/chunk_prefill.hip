@@ -329,10 +329,30 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+constexpr int64_t kPlanMaxN = 2048;
+
+// Relative cost of one chunk of a chain in the two-chains-per-CU kernel, with
+// the 8-wave kernel (one chain per CU) as 1: with another chain on its CU,
+// and alone on its CU (K = V = 128, bf16; measured on batches of equal
+// sequences).  The two-chains kernel is chosen only where its estimate is
+// below kTwoPerCuMargin of the 8-wave one.
+constexpr double kPairCost = 1.78, kLoneCost = 1.32, kTwoPerCuMargin = 0.95;
+
 // Ranks sequences by length, longest first (ties by index).  One workgroup.
+// With sel, it also picks the chunk kernel for the batch (H heads per
+// sequence, cus CUs), from makespan estimates in chunk units with chain i of
+// the batch (longest first) of c_i chunks and sum C:
+//   one chain per CU : max(C / cus, max_k (k + 1) c_{k cus}) -- among the
+//                      k cus + 1 longest chains some CU runs k + 1 in turn
+//   two chains per CU: max(kPairCost C / (2 cus), kLoneCost c_0)
+// and writes 1 (two chains per CU) or 0 to *sel.
 __global__ __launch_bounds__(1024) void plan_order_kernel(const int32_t* __restrict__ cu, int64_t N, int64_t T,
-                                                          int32_t* __restrict__ order) {
-  __shared__ int32_t len_s[2048];
+                                                          int64_t H, int32_t cus, int32_t* __restrict__ order,
+                                                          int32_t* __restrict__ sel) {
+  __shared__ int32_t len_s[kPlanMaxN];
+  __shared__ int32_t ord_s[kPlanMaxN];
+  __shared__ unsigned long long tot_s, lpt_s;
+  if (threadIdx.x == 0) tot_s = lpt_s = 0;
   for (int64_t s = threadIdx.x; s < N; s += blockDim.x) {
     int64_t b = cu[s], e = cu[s + 1];
     b = b < 0 ? 0 : (b > T ? T : b);
@@ -348,6 +368,26 @@ __global__ __launch_bounds__(1024) void plan_order_kernel(const int32_t* __restr
       rank += (lo > ls) || (lo == ls && o < s);
     }
     order[rank] = (int32_t)s;
+    ord_s[rank] = (int32_t)s;
+  }
+  if (!sel) return;  // (uniform)
+  __syncthreads();
+  unsigned long long part = 0;
+  for (int64_t s = threadIdx.x; s < N; s += blockDim.x) part += (unsigned long long)((len_s[s] + 63) / 64);
+  atomicAdd(&tot_s, part * (unsigned long long)H);
+  // chain i is one of the H heads of sequence ord_s[i / H]
+  const int64_t n = N * H;
+  for (int64_t k = threadIdx.x; k * cus < n; k += blockDim.x) {
+    const int64_t c = (len_s[ord_s[(k * cus) / H]] + 63) / 64;
+    atomicMax(&lpt_s, (unsigned long long)((k + 1) * c));
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const double mean = (double)tot_s / cus;
+    const double c0 = (double)((len_s[ord_s[0]] + 63) / 64);
+    const double one = fmax(mean, (double)lpt_s);
+    const double two = fmax(0.5 * kPairCost * mean, kLoneCost * c0);
+    *sel = two < kTwoPerCuMargin * one ? 1 : 0;
   }
 }
 
@@ -400,6 +440,10 @@ struct Params {
   int seg_role;
   const int32_t* seg_total;
   float* sin_next;
+  // kernel chosen on the device (NULL: none): a launch whose sel_want differs
+  // from *sel returns at once
+  const int32_t* sel;
+  int sel_want;
 };
 
 constexpr int kSegMaps = 1, kSegFirst = 2, kSegRest = 3;
@@ -1398,6 +1442,7 @@ __device__ __forceinline__ void chunk_body(const Params& p, char* smem) {
 template <int KP, int BV, bool kBF16, bool kSeg>
 __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) char smem[Cfg<KP, BV>::LDS];
+  if (p.sel && *p.sel != p.sel_want) return;
   chunk_body<KP, BV, kBF16, true, kSeg>(p, smem);
 }
 
@@ -1519,6 +1564,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prefill_2wg_kernel(Params p) {
   float* sDiag = reinterpret_cast<float*>(smem + R_DIAG);
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+  if (p.sel && *p.sel != p.sel_want) return;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63;
@@ -2182,8 +2228,6 @@ __global__ __launch_bounds__(256, 2) void chunk_prefill_2wg_kernel(Params p) {
   }
 }
 
-constexpr int64_t kPlanMaxN = 2048;
-
 // First-segment length for segments of lc tokens: a map chunk costs about
 // 0.8 of an output chunk (measured at K = V = 128, with both in one launch),
 // so a first segment of 0.8 lc tokens (its outputs, in pass 1) ends with the
@@ -2419,14 +2463,39 @@ __global__ __launch_bounds__(kScanT) void seg_scan_kernel(const int32_t* __restr
   }
 }
 
-// Batches of at least this many (sequence, head) chains with K = V = 128 and
-// bf16 q/k/v run two chains per CU (chunk_prefill_2wg_kernel), four chains
-// per CU of the 256.  With fewer, CUs sit at one chain or idle, and one chain
-// on 4 waves is about a third slower than on the 8 waves of
-// chunk_prefill_kernel (H = 32, K = V = 128: 4x8192 and 8x4096 tokens +31-35 %,
-// 16x2048 -6 %, 24x2048 +0 %, 32x2048 -8 %, 64x1024 -11 %, 200 sequences of
-// 64-8192 tokens -12 %).
+// K = V = 128 with bf16 q/k/v can run two chains per CU
+// (chunk_prefill_2wg_kernel).  Whether that pays depends on the batch: on a
+// CU of its own one chain of it is about a third slower than on the 8 waves of
+// chunk_prefill_kernel, and two on a CU take 1.78 of that time per chunk each
+// (H = 32, K = V = 128 against the 8-wave kernel: 8x4096 tokens +32 %, 12x4096
+// -13 %, 16x2048 -9 %, 20x2048 and 24x2048 -5 %, 32x2048 -8 %, 64x1024 -11 %,
+// 200 sequences of 64-8192 tokens -12 %; 16 sequences of 512-4096 tokens -2 %
+// to +17 %, as the longest chains share their CUs).  With more chains than
+// CUs the planning kernel chooses from the lengths and both kernels are
+// launched, the one not chosen returning at once; without a plan (one
+// sequence) the two-chains kernel runs from this many chains on.
 constexpr int64_t kTwoPerCuMinChains = 1024;
+
+bool two_per_cu_shape(const Params& prm, bool bf16) {
+  return bf16 && prm.K == 128 && prm.V == 128 && prm.pair && prm.ovec && prm.T <= INT32_MAX && prm.H <= 65535 &&
+         !prm.seq_of;
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static int cus[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cus[dev]) {
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+    cus[dev] = c;
+  }
+  return cus[dev];
+}
 
 template <int KP, int BV>
 hipError_t launch_cfg(const Params& prm, bool bf16, hipStream_t stream) {
@@ -2436,13 +2505,16 @@ hipError_t launch_cfg(const Params& prm, bool bf16, hipStream_t stream) {
   constexpr int nt = Cfg<KP, BV>::NT;
   const dim3 g3((unsigned)grid), b3(nt);
   if constexpr (KP == 128 && BV == 128) {
-    if (bf16 && prm.K == 128 && prm.V == 128 && prm.pair && prm.ovec && items >= kTwoPerCuMinChains &&
-        prm.T <= INT32_MAX && prm.H <= 65535 && !prm.seq_of) {
+    if (two_per_cu_shape(prm, bf16) && (prm.sel || items >= kTwoPerCuMinChains)) {
+      Params p2 = prm;
+      p2.sel_want = 1;
       if (prm.beta_bf16)
-        hipLaunchKernelGGL(chunk_prefill_2wg_kernel<true>, dim3((unsigned)items), dim3(w2::NT), 0, stream, prm);
+        hipLaunchKernelGGL(chunk_prefill_2wg_kernel<true>, dim3((unsigned)items), dim3(w2::NT), 0, stream, p2);
       else
-        hipLaunchKernelGGL(chunk_prefill_2wg_kernel<false>, dim3((unsigned)items), dim3(w2::NT), 0, stream, prm);
-      return hipGetLastError();
+        hipLaunchKernelGGL(chunk_prefill_2wg_kernel<false>, dim3((unsigned)items), dim3(w2::NT), 0, stream, p2);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess || !prm.sel) return e;
+      // (the 8-wave kernel below runs when the plan chose it)
     }
   }
   if (prm.seq_of) {
@@ -2556,7 +2628,7 @@ size_t chunk_prefill_workspace_bytes(int64_t T, int64_t N, int64_t H, int64_t K,
   const SegLayout L = seg_layout(T, N, H, K, V);
   if (L.seg_len) return L.total;
   if (N < 2 || N > kPlanMaxN) return 0;
-  return round256((size_t)N * 4);
+  return round256((size_t)N * 4 + 4);  // the order, the kernel choice
 }
 
 hipError_t launch_chunk_prefill(const kda_prefill_args_t& a, hipStream_t stream) {
@@ -2594,6 +2666,8 @@ hipError_t launch_chunk_prefill(const kda_prefill_args_t& a, hipStream_t stream)
   prm.seg_role = 0;
   prm.seg_total = nullptr;
   prm.sin_next = nullptr;
+  prm.sel = nullptr;
+  prm.sel_want = 0;
   const bool bf16 = a.qkv_dtype == KDA_BF16;
   hipError_t e;
 
@@ -2645,9 +2719,16 @@ hipError_t launch_chunk_prefill(const kda_prefill_args_t& a, hipStream_t stream)
 
   if (a.N >= 2 && a.N <= kPlanMaxN) {
     int32_t* order = static_cast<int32_t*>(a.workspace);
-    hipLaunchKernelGGL(plan_order_kernel, dim3(1), dim3(1024), 0, stream, a.cu_seqlens, a.N, a.T, order);
+    // more chains than CUs: the plan also picks the chunk kernel
+    Params pa = prm;
+    set_access_flags(pa);
+    const int cus = device_cus();
+    int32_t* sel = two_per_cu_shape(pa, bf16) && a.N * a.H > cus ? order + a.N : nullptr;
+    hipLaunchKernelGGL(plan_order_kernel, dim3(1), dim3(1024), 0, stream, a.cu_seqlens, a.N, a.T, a.H,
+                       (int32_t)cus, order, sel);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     prm.order = order;
+    prm.sel = sel;
   }
   return launch_variant(prm, bf16, stream);
 }

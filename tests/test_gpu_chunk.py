@@ -6,8 +6,8 @@ bf16 I/O, vector and element-by-element loads (odd K or V, sizes that are not
 a multiple of 4, unaligned tensors), no initial state, bf16 final states, out
 aliasing v, final states written in place over the initial states, strong
 decays that force shorter chunks, split/resume and determinism, on both
-kernels for K = V = 128 (one chain per CU below 1024 (sequence, head) chains,
-two per CU from there on).
+kernels for K = V = 128 (one chain per CU, or two, as the planning kernel
+chooses from the lengths once there are more chains than CUs).
 """
 import numpy as np
 import pytest
@@ -188,6 +188,33 @@ def test_two_chains_per_cu_bf16_beta():
     beta = bf16_tensor(bits).reshape(inp["beta"].shape)
     o, f = kda.kda_chunk_prefill(d["q"], d["k"], d["v"], d["g"], beta, d["cu_seqlens"], initial_state=d["initial"])
     torch.cuda.synchronize()
+    ro, rf = _ref(inp)
+    assert_chains(tensor_f64(o), ro, inp["cu_seqlens"], tensor_f64(f), rf)
+
+
+# More (sequence, head) chains than CUs with K = V = 128 and bf16 q/k/v: the
+# planning kernel picks the chunk kernel from the lengths and writes its choice
+# after the sequence order in the workspace (1: two chains per CU).
+@pytest.mark.parametrize("lengths,want", [
+    ([130] * 12, 1),                      # 384 chains of equal length: two per CU
+    ([2000] + [64] * 11, 0),              # one long sequence: its chains alone on their CUs
+    ([64 * 10] * 20 + [0, 1], 1),         # 704 chains, two empty and two single-token ones
+    ([3000, 2900] + [40] * 30, 0),        # 1024 chains, two long sequences
+])
+def test_planned_kernel_choice(lengths, want):
+    import torch
+    import kda_recurrent_state_amd as kda
+    H = 32
+    inp = wl.host_prefill_inputs(lengths, H, 128, 128, dtype="bf16", seed=64 + len(lengths))
+    print("case: planned kernel choice lengths=%s... H=%d want=%d" % (lengths[:3], H, want), flush=True)
+    d = device_inputs(inp)
+    N, T = len(lengths), sum(lengths)
+    ws = torch.full((kda.kda_chunk_prefill_workspace_size(T, N, H, 128, 128) // 4,), -1, dtype=torch.int32,
+                    device=d["q"].device)
+    o, f = kda.kda_chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"],
+                                 initial_state=d["initial"], workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws[N].item()) == want
     ro, rf = _ref(inp)
     assert_chains(tensor_f64(o), ro, inp["cu_seqlens"], tensor_f64(f), rf)
 
