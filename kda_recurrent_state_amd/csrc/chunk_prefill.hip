@@ -65,6 +65,7 @@ constexpr int kC = 64;  // chunk length
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRangeLimit = 100.f;
 constexpr float kL2Eps = 1e-6f;
+constexpr float kL2EpsLane = kL2Eps / 64;  // each lane's share of eps in a 64-lane row sum
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -195,7 +196,7 @@ __device__ __forceinline__ void rows_reduce(const float (&x)[R], float (&u)[R / 
   }
 }
 
-// out[r] = 1 / sqrt(sum over the wave's 64 lanes of x[r] + eps) for R rows at once,
+// out[r] = 1 / sqrt(sum over the wave's 64 lanes of x[r]) for R rows at once,
 // the same bits in every lane: one rsqrt per register of the reduce-scattered
 // sums covers four rows, and readlane hands each row to the wave.
 template <int R>
@@ -204,13 +205,13 @@ __device__ __forceinline__ void rows_rsqrt(const float (&x)[R], float (&out)[R])
   float u[R4];
   rows_reduce(x, u);
 #pragma unroll
-  for (int j = 0; j < R4; ++j) u[j] = __frsqrt_rn(u[j] + kL2Eps);
+  for (int j = 0; j < R4; ++j) u[j] = __frsqrt_rn(u[j]);
 #pragma unroll
   for (int r = 0; r < R; ++r) out[r] = lane_f(u[r % R4], 16 * (r / R4));
 }
 
 // Per-row factors of a wave's R chunk rows (rows row0 .. row0 + R - 1), from
-// each lane's shares of the row sums sk = |k|^2, sq = |q|^2 (eps is added to the sums)
+// each lane's shares of the row sums sk = |k|^2 (+ eps), sq = |q|^2 (+ eps)
 // and dq = k . q: rk[r] = 1 / |k_r| and rq[r] = 1 / |q_r| (1 without l2norm),
 // the same bits in every lane, and diag[r] = scale q^_r . k^_r, the
 // diagonal of A_qk, written by one lane per row.  That fp32 diagonal replaces
@@ -233,8 +234,8 @@ __device__ __forceinline__ void rows_norms_diag(const float (&sk)[R], const floa
     rows_reduce(sq, uq);
 #pragma unroll
     for (int j = 0; j < R4; ++j) {
-      uk[j] = __frsqrt_rn(uk[j] + kL2Eps);
-      uq[j] = __frsqrt_rn(uq[j] + kL2Eps);
+      uk[j] = __frsqrt_rn(uk[j]);
+      uq[j] = __frsqrt_rn(uq[j]);
       ud[j] *= uk[j] * uq[j];
     }
   }
@@ -886,21 +887,21 @@ __device__ __forceinline__ void chunk_body(const Params& p, char* smem) {
       }
     }
     // squared row norms of k and q and the dot products k . q (bf16 pairs: one
-    // dot2 per pair); eps is added once to the reduced norms
+    // dot2 per pair), each lane adding its share of eps to the norms
     float sk[RPW], sq[RPW], dq[RPW];
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       if (kBF16 && CPL == 2) {
         typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
         sk[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, raw.k[r][0]),
-                                                __builtin_bit_cast(bf16x2, raw.k[r][0]), 0.f, false);
+                                                __builtin_bit_cast(bf16x2, raw.k[r][0]), kL2EpsLane, false);
         sq[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, raw.q[r][0]),
-                                                __builtin_bit_cast(bf16x2, raw.q[r][0]), 0.f, false);
+                                                __builtin_bit_cast(bf16x2, raw.q[r][0]), kL2EpsLane, false);
         dq[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, raw.k[r][0]),
                                                 __builtin_bit_cast(bf16x2, raw.q[r][0]), 0.f, false);
       } else {
-        sk[r] = 0.f;
-        sq[r] = 0.f;
+        sk[r] = kL2EpsLane;
+        sq[r] = kL2EpsLane;
         dq[r] = 0.f;
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) {
@@ -1748,9 +1749,9 @@ __global__ __launch_bounds__(256, 2) void chunk_prefill_2wg_kernel(Params p) {
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       sk[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, rk_[r]), __builtin_bit_cast(bf16x2, rk_[r]),
-                                              0.f, false);
+                                              kL2EpsLane, false);
       sq[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, rq_[r]), __builtin_bit_cast(bf16x2, rq_[r]),
-                                              0.f, false);
+                                              kL2EpsLane, false);
       dq[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, rk_[r]), __builtin_bit_cast(bf16x2, rq_[r]),
                                               0.f, false);
     }
