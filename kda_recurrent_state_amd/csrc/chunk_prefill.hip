@@ -375,7 +375,8 @@ __global__ __launch_bounds__(1024) void plan_order_kernel(const int32_t* __restr
   __syncthreads();
   unsigned long long part = 0;
   for (int64_t s = threadIdx.x; s < N; s += blockDim.x) part += (unsigned long long)((len_s[s] + 63) / 64);
-  atomicAdd(&tot_s, part * (unsigned long long)H);
+  for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);  // one LDS atomic per wave
+  if ((threadIdx.x & 63) == 0 && part) atomicAdd(&tot_s, part * (unsigned long long)H);
   // chain i is one of the H heads of sequence ord_s[i / H]
   const int64_t n = N * H;
   for (int64_t k = threadIdx.x; k * cus < n; k += blockDim.x) {
