@@ -277,7 +277,14 @@ def test_checkpoint_offsets_helper():
 
 def test_workspace_size(lib):
     assert lib.kda_chunk_prefill_workspace_size(100, 1, 32, 128, 128) == 0
-    assert lib.kda_chunk_prefill_workspace_size(100, 200, 32, 128, 128) >= 800
+    # the planning kernel's sequence order (4 B per sequence) and its kernel
+    # choice (4 B after it), also when 4 N is a multiple of the 256-byte
+    # rounding
+    for n in (2, 64, 200, 2048):
+        ws = lib.kda_chunk_prefill_workspace_size(100, n, 32, 128, 128)
+        assert ws >= 4 * n + 4 and ws % 256 == 0
+    # more sequences than the planning kernel orders: natural order, no plan
+    assert lib.kda_chunk_prefill_workspace_size(10 ** 5, 2049, 32, 128, 128) == 0
 
 
 def test_status_strings(lib):
