@@ -21,8 +21,9 @@
 // consecutive elements, and the two row sums are 4-step DPP reductions within
 // those 16 lanes.  A workgroup of 256 threads owns one (n, h): 16 row groups,
 // each taking rows grp, grp+16, ... in batches of RB rows whose loads are all
-// issued before any arithmetic.  Only the raw row words stay in registers;
-// the decayed values are recomputed for the second pass.  The kernel moves
+// issued before any arithmetic.  The token's k, q and exp(g) are staged in
+// LDS once per workgroup.  Only the raw row words stay in registers; the
+// decayed values are recomputed for the second pass.  The kernel moves
 // 2 x K x V state elements per (n, h) and is HBM-bound.
 #include <type_traits>
 
@@ -179,38 +180,6 @@ __device__ __forceinline__ float dec_ldx(const void* base, uint32_t i) {
   return ldo<float>(base, 4u * i);
 }
 
-// This lane's EPL consecutive values of a q/k row (element offset c0).
-template <int EPL, bool kXB, bool kVec>
-__device__ __forceinline__ void load_x(const void* row, int c0, int K, float (&x)[EPL]) {
-  if constexpr (kVec) {
-    if constexpr (kXB) {
-      unsigned w[EPL / 2];
-      if constexpr (EPL == 4) {
-        const uint2 a = ldo<uint2>(row, 2u * c0);
-        w[0] = a.x; w[1] = a.y;
-      } else {
-        const uint4 a = ldo<uint4>(row, 2u * c0);
-        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-      }
-#pragma unroll
-      for (int e = 0; e < EPL; ++e)
-        x[e] = (e & 1) ? __uint_as_float(w[e >> 1] & 0xffff0000u) : __uint_as_float(w[e >> 1] << 16);
-    } else {
-#pragma unroll
-      for (int i = 0; i < EPL; i += 4) {
-        const float4 a = ldo<float4>(row, 4u * (c0 + i));
-        x[i] = a.x; x[i + 1] = a.y; x[i + 2] = a.z; x[i + 3] = a.w;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const int c = c0 + e;
-      x[e] = c < K ? dec_ldx<kXB>(row, (uint32_t)c) : 0.f;
-    }
-  }
-}
-
 // One batch of kRowGroups * kRB state rows starting at row v0 of one
 // (sequence, head): load, update in place, write the outputs.
 template <int EPL, bool kSB, bool kXB, bool kBB, bool kVec, typename XT>
@@ -229,15 +198,33 @@ __device__ __forceinline__ void decode_batch(const DecodeParams& p, int64_t item
     vv[i] = dec_ldx<kXB>(vrow, (uint32_t)row);
   }
   const float b = dec_ldx<kBB>(p.beta, (uint32_t)item);
-  // key-side values of this lane's EPL columns
+  // key-side values of this lane's EPL columns: k, q and exp(g) staged in LDS
+  // once per workgroup (loading them in every row group repeated a third of
+  // the workgroup's load instructions and the exponentials 16 times)
+  __shared__ __attribute__((aligned(16))) float sx[3][16 * EPL];
+  if (v0 == 0) {
+    const int t = threadIdx.x;
+    if (t < 16 * EPL) {
+      const bool in = t < K;
+      sx[0][t] = in ? dec_ldx<kXB>(krow, (uint32_t)t) : 0.f;
+      sx[1][t] = in ? dec_ldx<kXB>(qrow, (uint32_t)t) : 0.f;
+      sx[2][t] = in ? __builtin_amdgcn_exp2f(grow[t] * kDecLog2e) : 0.f;
+    }
+    __syncthreads();
+  }
   float kh[EPL], qh[EPL], dk[EPL];
-  load_x<EPL, kXB, kVec>(krow, EPL * j, K, kh);
-  load_x<EPL, kXB, kVec>(qrow, EPL * j, K, qh);
-  load_x<EPL, false, kVec>(grow, EPL * j, K, dk);
+#pragma unroll
+  for (int e = 0; e < EPL; e += 4) {
+    const float4 a = *reinterpret_cast<const float4*>(&sx[0][EPL * j + e]);
+    const float4 c = *reinterpret_cast<const float4*>(&sx[1][EPL * j + e]);
+    const float4 d = *reinterpret_cast<const float4*>(&sx[2][EPL * j + e]);
+    kh[e] = a.x; kh[e + 1] = a.y; kh[e + 2] = a.z; kh[e + 3] = a.w;
+    qh[e] = c.x; qh[e + 1] = c.y; qh[e + 2] = c.z; qh[e + 3] = c.w;
+    dk[e] = d.x; dk[e + 1] = d.y; dk[e + 2] = d.z; dk[e + 3] = d.w;
+  }
   float sk = 0.f, sq = 0.f;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
-    dk[e] = EPL * j + e < K ? __builtin_amdgcn_exp2f(dk[e] * kDecLog2e) : 0.f;
     sk += kh[e] * kh[e];
     sq += qh[e] * qh[e];
   }
