@@ -30,9 +30,11 @@
  *       K^-1/2 and the output allowed to reuse v's buffer.
  *
  * Conventions shared by every entry point:
- *  - Ownership: the library owns no memory.  The caller allocates every
- *    buffer (device memory unless stated) and passes the HIP stream on each
- *    call; nothing is retained between calls.
+ *  - Ownership: the library owns no memory (except the static scratch of
+ *    kda_chunk_prefill_noalloc).  The caller allocates every buffer (device
+ *    memory unless stated) and passes the HIP stream on each call; no buffer
+ *    or per-call state is retained between calls (the library looks up each
+ *    device's CU count, and the scratch's address, once).
  *  - stream: a hipStream_t passed as void* (NULL = the default stream).  All
  *    work is enqueued on it; no entry point synchronises the device or reads
  *    device memory on the host.
