@@ -219,6 +219,22 @@ def test_planned_kernel_choice(lengths, want):
     assert_chains(tensor_f64(o), ro, inp["cu_seqlens"], tensor_f64(f), rf)
 
 
+def test_two_per_cu_batches_take_the_two_chains_kernel():
+    """The batches the two-chains tests (here and in test_gpu_checkpoints.py)
+    rely on are planned onto that kernel."""
+    import torch
+    import kda_recurrent_state_amd as kda
+    for lengths in (TWO_PER_CU, [0, 1, 64, 65, 300] + [40 + 7 * i for i in range(59)]):
+        inp = wl.host_prefill_inputs(lengths, 16, 128, 128, dtype="bf16", seed=65)
+        d = device_inputs(inp)
+        N, T = len(lengths), sum(lengths)
+        ws = torch.full((kda.kda_chunk_prefill_workspace_size(T, N, 16, 128, 128) // 4,), -1, dtype=torch.int32,
+                        device=d["q"].device)
+        kda.kda_chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[N].item()) == 1, lengths[:6]
+
+
 def test_zero_length_sequences_pass_state_through():
     inp = wl.host_prefill_inputs([5, 0, 70, 0], 2, 64, 64, dtype="bf16", seed=7)
     o, f = _run(inp)
