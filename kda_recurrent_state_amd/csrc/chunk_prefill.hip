@@ -2506,6 +2506,9 @@ hipError_t launch_cfg(const Params& prm, bool bf16, hipStream_t stream) {
   const int64_t grid = groups * 8 * prm.nvb;
   constexpr int nt = Cfg<KP, BV>::NT;
   const dim3 g3((unsigned)grid), b3(nt);
+  // the 8-wave kernel obeys the plan's choice only beside the two-chains one
+  Params p8 = prm;
+  p8.sel = nullptr;
   if constexpr (KP == 128 && BV == 128) {
     if (two_per_cu_shape(prm, bf16) && (prm.sel || items >= kTwoPerCuMinChains)) {
       Params p2 = prm;
@@ -2516,19 +2519,21 @@ hipError_t launch_cfg(const Params& prm, bool bf16, hipStream_t stream) {
         hipLaunchKernelGGL(chunk_prefill_2wg_kernel<false>, dim3((unsigned)items), dim3(w2::NT), 0, stream, p2);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess || !prm.sel) return e;
-      // (the 8-wave kernel below runs when the plan chose it)
+      // the 8-wave kernel below runs when the plan chose it
+      p8.sel = prm.sel;
+      p8.sel_want = 0;
     }
   }
   if (prm.seq_of) {
     if (bf16)
-      hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, true, true>), g3, b3, 0, stream, prm);
+      hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, true, true>), g3, b3, 0, stream, p8);
     else
-      hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, false, true>), g3, b3, 0, stream, prm);
+      hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, false, true>), g3, b3, 0, stream, p8);
   } else {
     if (bf16)
-      hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, true, false>), g3, b3, 0, stream, prm);
+      hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, true, false>), g3, b3, 0, stream, p8);
     else
-      hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, false, false>), g3, b3, 0, stream, prm);
+      hipLaunchKernelGGL((chunk_prefill_kernel<KP, BV, false, false>), g3, b3, 0, stream, p8);
   }
   return hipGetLastError();
 }
