@@ -102,12 +102,16 @@ struct Cfg {
   static constexpr int SZ_A = kC * LDA * 2;
   static constexpr int SZ_KB = KP * kC * 2;  // Kbar^T: unpadded rows, 16-byte runs swizzled (kb_pos)
   // LDS map (bytes).  KL, QL and KR die after the A products; QL's space is
-  // reused for -W and KR's for the output staging tile.
-  static constexpr int R_KL = 0;                    // KL [64][KP]
+  // reused for -W and KR's for the output staging tile.  With KP = 64, Qg
+  // is held in registers through phase B and then written over KL, and the
+  // gate totals share the fp32 diagonal blocks' region, so that a workgroup
+  // fits in 80 KiB and two share a CU.
+  static constexpr bool kCompact = KP == 64;
+  static constexpr int R_KL = 0;                    // KL [64][KP]      (-> Qg when compact)
   static constexpr int R_QL = R_KL + SZ_ROW;        // QL [64][KP]      -> -W [64][KP]
   static constexpr int R_KR = R_QL + SZ_ROW;        // KR [64][KP]      -> O staging [64][BV]
-  static constexpr int R_QG = R_KR + SZ_ROW;        // Qg [64][KP]
-  static constexpr int R_KE = R_QG + SZ_ROW;        // (beta K 2^gamma)^T [KP][64]
+  static constexpr int R_QG = kCompact ? R_KL : R_KR + SZ_ROW;  // Qg [64][KP]
+  static constexpr int R_KE = R_KR + SZ_ROW + (kCompact ? 0 : SZ_ROW);  // (beta K 2^gamma)^T [KP][64]
   static constexpr int R_KB = R_KE + SZ_KT;         // Kbar^T [KP][64]
   static constexpr int R_VT = R_KB + SZ_KB;         // (beta V)^T [BV][64]
   static constexpr int R_AB = R_VT + SZ_VT;         // bf16 [64][LDT]: -A_kk below the diagonal blocks, D_b on them
@@ -117,12 +121,13 @@ struct Cfg {
   static constexpr int AD_C = 20, AD_B = 16 * AD_C + 4;
   static constexpr int R_AD = R_AB + SZ_T;
   static constexpr int R_AQK = R_AD + 4 * AD_B * 4;  // A_qk bf16 [64][LDA]
-  static constexpr int R_TOT = R_AQK + SZ_A;        // per-wave gate sums fp32 [NW][KP]
-  static constexpr int R_DEC = R_TOT + NW * KP * 4; // 2^gamma_L fp32 [KP]
+  static constexpr int R_TOT = kCompact ? R_AD : R_AQK + SZ_A;  // per-wave gate sums fp32 [NW][KP]
+  static constexpr int R_DEC = R_AQK + SZ_A + (kCompact ? 0 : NW * KP * 4);  // 2^gamma_L fp32 [KP]
   static constexpr int R_RED = R_DEC + KP * 4;      // range guard fp32 [NW]
   static constexpr int R_DIAG = R_RED + 64;         // fp32 [64] diagonal of A_qk
   static constexpr int LDS = R_DIAG + kC * 4;
   static_assert(LDS <= 160 * 1024, "LDS budget");
+  static_assert(!kCompact || (LDS <= 80 * 1024 && NW * KP * 4 <= 4 * AD_B * 4), "two workgroups per CU");
   static_assert(kC * LDO * 2 <= SZ_ROW, "output staging fits in the KR region");
   static_assert(RPW == 8 || RPW == 16, "rows per wave");
 };
@@ -997,6 +1002,7 @@ __device__ __forceinline__ void chunk_body(const Params& p, char* smem) {
     if (l == 0) sRed[w] = guard;  // checked after phase A's barrier
 
     // ---------------- phase A: gated operand tiles into LDS ----------------
+    __bf16 qgh[C::kCompact ? RPW : 1];  // Qg of this lane's channel, stored after phase B (compact map)
     {
       float cg[CPL], cb[CPL];
 #pragma unroll
@@ -1042,7 +1048,10 @@ __device__ __forceinline__ void chunk_body(const Params& p, char* smem) {
           sKR[i * C::LDK + c_lo] = kr[0];
           if constexpr (kOut) {
             sQL[i * C::LDK + c_lo] = ql[0];
-            sQg[i * C::LDK + kpos((int)c_lo)] = qg[0];
+            if constexpr (C::kCompact)
+              qgh[r] = qg[0];
+            else
+              sQg[i * C::LDK + kpos((int)c_lo)] = qg[0];
           }
         }
       }
@@ -1200,6 +1209,12 @@ __device__ __forceinline__ void chunk_body(const Params& p, char* smem) {
     // the other half's loads (they land while phases D-E compute)
     if (!early && t0 + L < len) issue_loads(t0 + L, w);
     lds_barrier();
+    if constexpr (kOut && C::kCompact) {
+      // Qg over KL, which phase B has finished reading; phase E reads it
+      // after phase D's barrier
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) sQg[(RPW * w + r) * C::LDK + kpos((int)c_lo)] = qgh[r];
+    }
 
     // ---------------- phase D: [W | U] = (I + A_kk)^-1 [beta K 2^gamma | beta V] --
     // Blocked forward substitution, one 16-column tile at a time, no barriers:
@@ -1442,7 +1457,7 @@ __device__ __forceinline__ void chunk_body(const Params& p, char* smem) {
 }
 
 template <int KP, int BV, bool kBF16, bool kSeg>
-__global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
+__global__ __launch_bounds__(BV * 4, (Cfg<KP, BV>::kCompact ? 2 : 1)) void chunk_prefill_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) char smem[Cfg<KP, BV>::LDS];
   if (p.sel && *p.sel != p.sel_want) return;
   chunk_body<KP, BV, kBF16, true, kSeg>(p, smem);
@@ -1455,7 +1470,7 @@ __global__ __launch_bounds__(BV * 4) void chunk_prefill_kernel(Params p) {
 // work-item mapping of chunk_body gives the same segment for a workgroup
 // under either.
 template <int KP, int BV, bool kBF16>
-__global__ __launch_bounds__(BV * 4) void chunk_prefill_seg1_kernel(Params pout, Params pmap) {
+__global__ __launch_bounds__(BV * 4, (Cfg<KP, BV>::kCompact ? 2 : 1)) void chunk_prefill_seg1_kernel(Params pout, Params pmap) {
   __shared__ __attribute__((aligned(16))) char smem[Cfg<KP, BV>::LDS];
   const int64_t b = blockIdx.x;
   const int64_t grp = b / (8 * pout.nvb);
