@@ -56,7 +56,7 @@ def test_tiny_fp32():
     _check(inp)
 
 
-@pytest.mark.parametrize("K,V", [(64, 32), (32, 64), (128, 64), (128, 128), (48, 80), (128, 200)])
+@pytest.mark.parametrize("K,V", [(64, 32), (32, 64), (128, 64), (128, 128), (48, 80), (128, 200), (96, 40)])
 def test_shapes_k_ne_v(K, V):
     inp = wl.host_prefill_inputs([70, 130], 2, K, V, dtype="bf16", seed=K * 1000 + V)
     _check(inp)
