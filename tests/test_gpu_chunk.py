@@ -145,9 +145,9 @@ def test_many_chains_take_full_value_blocks():
     _check(inp)
 
 
-# Two chains per CU (K = V = 128, bf16 q/k/v, at least 1024 (sequence, head)
-# chains): 64 ragged sequences, among them empty, single-token and exact
-# chunk-multiple ones, x 16 heads.
+# Two chains per CU (K = V = 128, bf16 q/k/v, 1024 (sequence, head) chains
+# that the planning kernel puts two to a CU): 64 ragged sequences, among them
+# empty, single-token and exact chunk-multiple ones, x 16 heads.
 TWO_PER_CU = [0, 1, 64, 65, 128] + [40 + 3 * i for i in range(59)]
 
 
@@ -272,7 +272,7 @@ def test_single_token():
 @pytest.mark.parametrize("gval", [-30.0, -1e4])
 @pytest.mark.parametrize("lengths,H,K,V", [
     ([150, 70], 2, 64, 64),                            # K <= 64 kernel
-    ([150, 70], 2, 128, 64),                           # 64-column value blocks (V <= 64)
+    ([150, 70], 2, 128, 64),                           # 128-column value block, V = 64
     ([150, 70], 2, 128, 128),                          # 128-column value blocks, few chains
     ([130 + 5 * (i % 7) for i in range(64)], 8, 128, 128),  # 128-column value blocks, 512 chains
 ])
